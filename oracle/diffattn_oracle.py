@@ -1,0 +1,206 @@
+"""Oracle for the fused differential-attention forward.
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only ``tests/``,
+``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may
+import or call this module.  It shares no code with the HIP path and imports
+nothing from the package.
+
+Everything here is plain NumPy in float64: slow, obviously correct, written
+straight from the definitions on the source pages.  Citations name the page
+and the section / equation they follow:
+
+* page 1 = "Differential Transformer: Canceling Context Noise with Differential
+  Attention" (priorstack.com), section "Cancelling Context Noise Through
+  Attention Map Subtraction" -- the DiffAttn formula (Eq. 1) and the lambda
+  re-parameterisation (Eq. 2).
+* page 2 = "Differential attention" (datarekha.com), section "The
+  noise-canceling idea" -- the formula again, the numerically stable softmax of
+  the worked six-key example, and the printed example values.
+* page 3 = "Differential Transformer" sample peer review (reviewpaper.ai),
+  "Summary" (Eq. 1, Eq. 2 and Eq. 3: per-head normalisation followed by the
+  fixed (1 - lambda_init) factor) and "Weaknesses" (head-wise RMSNorm; rows of
+  the differential map sum to 1 - lambda; lambda is unconstrained).
+
+Readings taken where the pages are silent (each is listed with its reason in
+the design notes of the repository):
+
+* the per-head normaliser is RMSNorm over the 2d value channels, without mean
+  subtraction or bias, with eps added inside the square root;
+* the RMSNorm weight has shape [2d] and is shared by all heads;
+* the 1/sqrt(d) scale uses the per-map query/key width d (not 2d);
+* lambda is one scalar per call, shared by all heads and tokens;
+* causal means key j is visible to query i iff j <= i (diagonal included);
+* decode attends the first cache_len[b] cached keys; a sequence with
+  cache_len 0 attends nothing and its output is defined as zero.
+
+Every function below is pinned by ``tests/test_oracle.py`` against facts that
+do not come from this file: the printed example values, closed forms,
+invariants, and library routines (torch's scaled_dot_product_attention and
+rms_norm, in float64 on the CPU).
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "lambda_scalar",
+    "softmax_rows",
+    "attention_map",
+    "diff_weights",
+    "pre_norm",
+    "head_rmsnorm_scale",
+    "forward",
+    "forward_rows",
+    "decode",
+]
+
+
+def _f64(x) -> np.ndarray:
+    """Upcast to float64 exactly (bf16 and fp32 values are representable)."""
+    if hasattr(x, "detach"):  # a torch tensor: go through float32/float64 on the CPU
+        x = x.detach().to("cpu")
+        import torch  # local import: torch is only plumbing for readback
+
+        x = x.to(torch.float64).numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def lambda_scalar(lq1, lk1, lq2, lk2, lambda_init: float) -> float:
+    """lambda = exp(lq1 . lk1) - exp(lq2 . lk2) + lambda_init.
+
+    Page 1, "Cancelling Context Noise Through Attention Map Subtraction" (the
+    re-parameterisation); page 3, "Summary", Eq. 2.
+    """
+    lq1, lk1, lq2, lk2 = (_f64(v) for v in (lq1, lk1, lq2, lk2))
+    return float(math.exp(float(np.dot(lq1, lk1))) - math.exp(float(np.dot(lq2, lk2))) + float(lambda_init))
+
+
+def softmax_rows(s: np.ndarray) -> np.ndarray:
+    """Softmax along the last axis, made stable by subtracting the row maximum.
+
+    Page 2, "The noise-canceling idea": the example subtracts the maximum before
+    exponentiating.  Entries equal to -inf (masked keys) get weight exactly 0.
+    """
+    m = np.max(s, axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def _visible(nq: int, nk: int, causal: bool, q_pos=None) -> np.ndarray:
+    """Boolean [nq, nk]: may query row r see key j?
+
+    Causal reading: the query at absolute position p sees key j iff j <= p.
+    ``q_pos`` gives each row's absolute position (default 0..nq-1).
+    """
+    if not causal:
+        return np.ones((nq, nk), dtype=bool)
+    pos = np.arange(nq) if q_pos is None else np.asarray(q_pos)
+    return np.arange(nk)[None, :] <= pos[:, None]
+
+
+def attention_map(q: np.ndarray, k: np.ndarray, causal: bool, q_pos=None) -> np.ndarray:
+    """softmax(Q K^T / sqrt(d)) for one head.  q: [nq, d], k: [nk, d].
+
+    Page 1 / page 2 (Eq. 1): each map is a softmax of scaled dot products; d is
+    the query/key width of that map.
+    """
+    q, k = _f64(q), _f64(k)
+    d = q.shape[-1]
+    s = (q @ k.T) / math.sqrt(d)
+    s = np.where(_visible(q.shape[0], k.shape[0], causal, q_pos), s, -np.inf)
+    return softmax_rows(s)
+
+
+def diff_weights(q1, k1, q2, k2, lam: float, causal: bool, q_pos=None) -> np.ndarray:
+    """The differential map D = softmax(Q1 K1^T/sqrt d) - lambda softmax(Q2 K2^T/sqrt d).
+
+    Page 1 and page 2, Eq. 1; page 3 "Summary", Eq. 1.  Entries may be
+    negative and each row sums to 1 - lambda (page 3, "Weaknesses").
+    """
+    return attention_map(q1, k1, causal, q_pos) - float(lam) * attention_map(q2, k2, causal, q_pos)
+
+
+def pre_norm(q1, k1, q2, k2, v, lam: float, causal: bool, q_pos=None) -> np.ndarray:
+    """Y = D V for one head: the DiffAttn output before normalisation (Eq. 1)."""
+    return diff_weights(q1, k1, q2, k2, lam, causal, q_pos) @ _f64(v)
+
+
+def head_rmsnorm_scale(y, weight, eps: float, lambda_init: float) -> np.ndarray:
+    """out = (1 - lambda_init) * w * y / sqrt(mean(y^2) + eps) over the last axis.
+
+    Page 3, "Summary", Eq. 3 (per-head normalisation, then the fixed
+    (1 - lambda_init) factor) and "Weaknesses" (head-wise RMSNorm).
+    """
+    y = _f64(y)
+    w = np.ones(y.shape[-1]) if weight is None else _f64(weight)
+    ms = np.mean(y * y, axis=-1, keepdims=True)
+    return (1.0 - float(lambda_init)) * (w * y) / np.sqrt(ms + float(eps))
+
+
+def forward(q1, k1, q2, k2, v, lam: float, lambda_init: float, weight=None,
+            eps: float = 1e-5, causal: bool = True, norm: bool = True,
+            block: int = 512) -> np.ndarray:
+    """Multi-head differential attention forward.
+
+    q1, k1, q2, k2: [B, H, N, d]; v: [B, H, N, 2d]  ->  out [B, H, N, 2d].
+    With ``norm=False`` returns Y = D V (Eq. 1) instead of Eq. 3's output.
+    Query rows are processed ``block`` at a time to bound memory; blocking
+    does not change any value (each row is independent).
+    """
+    q1, k1, q2, k2, v = (_f64(t) for t in (q1, k1, q2, k2, v))
+    B, H, N, _ = q1.shape
+    out = np.empty(v.shape[:3] + (v.shape[-1],), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            for r0 in range(0, N, block):
+                rows = np.arange(r0, min(N, r0 + block))
+                y = pre_norm(q1[b, h, rows], k1[b, h], q2[b, h, rows], k2[b, h], v[b, h],
+                             lam, causal, q_pos=rows)
+                out[b, h, rows] = head_rmsnorm_scale(y, weight, eps, lambda_init) if norm else y
+    return out
+
+
+def forward_rows(q1, k1, q2, k2, v, rows, lam: float, lambda_init: float,
+                 weight=None, eps: float = 1e-5, causal: bool = True,
+                 norm: bool = True) -> np.ndarray:
+    """Outputs of the given query rows only, for one head.
+
+    q1, k1, q2, k2: [N, d]; v: [N, 2d]; rows: 1-D int array.  Each row is
+    computed against its full (causal) key prefix, exactly as in ``forward``.
+    Used to check sampled outputs at sizes where the full oracle is too slow.
+    """
+    rows = np.asarray(rows)
+    kmax = int(rows.max()) + 1 if causal else _f64(k1).shape[0]
+    k1, k2, v = _f64(k1)[:kmax], _f64(k2)[:kmax], _f64(v)[:kmax]
+    y = pre_norm(_f64(q1)[rows], k1, _f64(q2)[rows], k2, v, lam, causal, q_pos=rows)
+    return head_rmsnorm_scale(y, weight, eps, lambda_init) if norm else y
+
+
+def decode(q1, q2, k1c, k2c, vc, cache_len, lam: float, lambda_init: float,
+           weight=None, eps: float = 1e-5, norm: bool = True) -> np.ndarray:
+    """One query token per sequence against a KV cache.
+
+    q1, q2: [B, H, d]; k1c, k2c: [B, H, L, d]; vc: [B, H, L, 2d];
+    cache_len: [B] ints (None = L).  Sequence b attends cached keys
+    [0, cache_len[b]) with no mask (the new token's keys are already in the
+    cache).  Same maths as ``forward`` with one query row (Eq. 1-3).
+    A sequence with cache_len 0 gives zeros (reading: nothing to attend to).
+    """
+    q1, q2 = _f64(q1), _f64(q2)
+    B, H, d = q1.shape
+    L = k1c.shape[2]
+    dv = vc.shape[-1]
+    lens = np.full(B, L) if cache_len is None else np.asarray(cache_len).astype(np.int64)
+    out = np.zeros((B, H, dv))
+    for b in range(B):
+        n = int(min(max(lens[b], 0), L))
+        if n == 0:
+            continue
+        for h in range(H):
+            y = pre_norm(q1[b, h][None], _f64(k1c[b, h, :n]), q2[b, h][None], _f64(k2c[b, h, :n]),
+                         _f64(vc[b, h, :n]), lam, causal=False)
+            out[b, h] = (head_rmsnorm_scale(y, weight, eps, lambda_init) if norm else y)[0]
+    return out
