@@ -1,0 +1,213 @@
+"""Benchmark of the differential-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step = diffattn_lambda + diffattn_fwd over the 1.4B-scale layer workload
+(bf16, B=4, H=16, N=2048, d=64, V width 128, causal).  Prints ONE JSON line:
+the whole-step throughput in TFLOP/s (12 d flops per causal query/key pair),
+the prefill kernel's roofline fraction against the bf16 dense MFMA peak, the
+CPU fp64 oracle timed on a bounded sample of the same workload, and a decode
+leg (diffattn_decode on 64 sequences x 16 heads x 32768 cached keys, d=128)
+reported in HBM GB/s against the 8 TB/s peak.  Inputs are seeded synthetic
+tensors already resident in HBM when timing starts.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "diff-attn fwd TFLOP/s & % bf16 MFMA peak (prefill); decode HBM GB/s & % peak"
+
+
+def _src_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "transformer_attention_diffattn_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kind: str, src: str):
+    """Per-launch HBM bytes from the committed counter summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kind}_traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except OSError:
+        return None
+    return t.get("bytes_per_launch") if t.get("source_sha256_16") == _src_hash(src) else None
+
+
+def _timed_loop(fn, steps, stream, torch):
+    """Run fn() `steps` times; returns (total ms, list of per-launch ms of the
+    event pair fn brackets itself with)."""
+    per = []
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(steps):
+        per.append(fn())
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1), [a.elapsed_time(b) for a, b in per]
+
+
+def cpu_baseline(x, w, budget_s: float):
+    """The oracle as it stands, on whole heads of the same inputs, until
+    ``budget_s`` seconds of host time are spent."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import diffattn_oracle as O
+
+    lam = O.lambda_scalar(x["lq1"].cpu(), x["lk1"].cpu(), x["lq2"].cpu(), x["lk2"].cpu(), x["lambda_init"])
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    done = 0
+    t0 = time.perf_counter()
+    for b, h in heads:
+        sl = lambda t: t[b:b + 1, h:h + 1].cpu()
+        O.forward(sl(x["q1"]), sl(x["k1"]), sl(x["q2"]), sl(x["k2"]), sl(x["v"]), lam, x["lambda_init"],
+                  eps=x["eps"], causal=w.causal)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = 12.0 * w.d * w.pairs() * done
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {len(heads)} heads of the same workload, every causal row, "
+                      f"fp64 NumPy, {dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=10)
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode leg")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of CPU oracle time")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="also run one device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the path has no multi-GPU leg "
+              "(every (batch, head) is independent; sharding is described in the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from transformer_attention_diffattn_amd import binding as da
+    from transformer_attention_diffattn_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+
+    # ---------------- prefill: the headline workload
+    w = W.WORKLOADS[W.HEADLINE_PREFILL]
+    x = W.workload_inputs(w.name, device=dev)
+    lam_t = torch.empty(1, device=dev, dtype=torch.float32)
+    out = torch.empty_like(x["v"])
+
+    def step():
+        da.lam(x["lq1"], x["lk1"], x["lq2"], x["lk2"], x["lambda_init"], out=lam_t)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        da.fwd(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam_t, x["lambda_init"], eps=x["eps"],
+               causal=w.causal, out=out)
+        e1.record(stream)
+        return e0, e1
+
+    for _ in range(args.warmup):
+        step()
+    total_ms, per = _timed_loop(step, args.steps, stream, torch)
+    if not torch.isfinite(out.float()).all():
+        raise RuntimeError("non-finite prefill output")
+    ms_step = total_ms / args.steps
+    kern_ms = sum(per) / len(per)
+    flops = 12.0 * w.d * w.pairs() * w.B * w.H
+    value = flops / (ms_step * 1e-3) / 1e12
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    res = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "v_width": 2 * w.d,
+                   "causal": w.causal, "lambda_init": x["lambda_init"],
+                   "flops_per_pair": 12 * w.d, "pairs_per_head": w.pairs()},
+        "roofline": {"bound": "mfma", "kernel": "prefill_bf16_kernel<64,causal,norm>",
+                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": _traffic("prefill_layer1p4b", "prefill.hip"),
+                     "kernel_ms": round(kern_ms, 4)},
+    }
+
+    # ---------------- decode leg
+    if not args.no_decode:
+        del out
+        wd = W.WORKLOADS[W.HEADLINE_DECODE]
+        y = W.workload_inputs(wd.name, device=dev)
+        lam_d = da.lam(y["lq1"], y["lk1"], y["lq2"], y["lk2"], y["lambda_init"])
+        ws = torch.empty(da.decode_workspace_bytes(wd.B, wd.H, wd.N, wd.d), dtype=torch.uint8, device=dev)
+        outd = torch.empty((wd.B, wd.H, 1, 2 * wd.d), dtype=torch.bfloat16, device=dev)
+
+        def dstep():
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            da.decode(y["q1"], y["q2"], y["k1c"], y["k2c"], y["vc"], lam_d, y["lambda_init"],
+                      cache_len=y["cache_len"], eps=y["eps"], workspace=ws, out=outd)
+            e1.record(stream)
+            return e0, e1
+
+        for _ in range(2):
+            dstep()
+        dtotal, dper = _timed_loop(dstep, args.decode_steps, stream, torch)
+        dms = sum(dper) / len(dper)
+        nbytes = wd.B * wd.H * wd.N * 8 * wd.d  # K1 + K2 + V per cached key, bf16
+        gbs = nbytes / (dms * 1e-3) / 1e9
+        res["decode"] = {
+            "workload": wd.name, "B": wd.B, "H": wd.H, "L": wd.N, "d": wd.d,
+            "ms_per_step": round(dtotal / args.decode_steps, 4),
+            "roofline": {"bound": "hbm", "kernel": "decode_split_kernel<bf16,128> + decode_merge_kernel",
+                         "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": _traffic("decode_l32k", "decode.hip"),
+                         "algorithmic_bytes": nbytes, "kernel_ms": round(dms, 4)},
+        }
+        del y, ws
+
+    if args.copy_calib_mib > 0:
+        n = args.copy_calib_mib * (1 << 20)
+        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        res["copy_calibration_bytes"] = n
+
+    # ---------------- CPU oracle on a bounded sample of the same workload
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(x, w, args.cpu_budget)
+
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,143 @@
+/*
+ * diffattn.h -- C ABI of libdiffattn.so: the fused differential-attention
+ * forward for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (per batch b, head h, query row i):
+ *
+ *   lambda = exp(lq1 . lk1) - exp(lq2 . lk2) + lambda_init            (Eq. 2)
+ *   D      = softmax(Q1 K1^T / sqrt(d)) - lambda softmax(Q2 K2^T / sqrt(d))
+ *   Y      = D V                                                     (Eq. 1)
+ *   out    = (1 - lambda_init) * w * Y / sqrt(mean_{2d}(Y^2) + eps)   (Eq. 3)
+ *
+ * Sources: "Differential Transformer: Canceling Context Noise with
+ * Differential Attention" (priorstack.com), section "Cancelling Context Noise
+ * Through Attention Map Subtraction" (Eq. 1 and the lambda formula);
+ * "Differential attention" (datarekha.com), section "The noise-canceling
+ * idea" (Eq. 1, stable softmax) and "How it's wired" (Q/K split in halves, V
+ * twice as wide); the "Differential Transformer" sample review
+ * (reviewpaper.ai), "Summary" (Eq. 1-3: per-head normalisation and the fixed
+ * (1 - lambda_init) factor) and "Weaknesses" (head-wise RMSNorm, V width 2d).
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers (HIP), owned by the caller; the
+ *    library allocates nothing and keeps no state between calls.
+ *  - Tensors are dense, contiguous, row-major, in the shapes given, and each
+ *    pointer is 16-byte aligned.  `dt` gives the element type of q/k/v/out
+ *    and of the caches; lambda vectors, lambda, the norm weight are fp32.
+ *  - d is the per-map query/key width and must be 16, 32, 64 or 128; the
+ *    value width is exactly 2d.  The 1/sqrt(d) scale uses that d.
+ *  - Arguments are validated before any HIP call.  A bad argument returns
+ *    DIFFATTN_EINVAL / DIFFATTN_EUNSUPPORTED / DIFFATTN_EWORKSPACE and
+ *    launches nothing.  A failed launch returns DIFFATTN_EHIP.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *    and runs asynchronously; faults surface at the caller's next sync.
+ *  - Empty work (B, H or N equal to 0; for decode B or H) is valid: the call
+ *    returns DIFFATTN_OK without inspecting pointers or launching anything.
+ *  - Reads of the inputs and writes of the outputs never overlap: `out` must
+ *    not alias any input.
+ */
+#ifndef DIFFATTN_H
+#define DIFFATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DIFFATTN_ABI_VERSION 1
+
+#if defined(__GNUC__) || defined(__clang__)
+#define DIFFATTN_API __attribute__((visibility("default")))
+#else
+#define DIFFATTN_API
+#endif
+
+typedef enum {
+  DIFFATTN_OK = 0,
+  DIFFATTN_EINVAL = 1,       /* null/misaligned pointer, negative size, bad flag  */
+  DIFFATTN_EUNSUPPORTED = 2, /* d or dtype outside the supported set              */
+  DIFFATTN_EHIP = 3,         /* a HIP launch or query failed                      */
+  DIFFATTN_EWORKSPACE = 4    /* decode workspace missing or too small             */
+} diffattn_status;
+
+typedef enum { DIFFATTN_FP32 = 0, DIFFATTN_BF16 = 1 } diffattn_dtype;
+
+/* Key j is visible to query i iff j <= i (diagonal included). */
+#define DIFFATTN_CAUSAL 1u
+/* Emit Y = D V (Eq. 1 output) and skip the RMSNorm and the scale.  A testing
+ * hook: lambda_init, norm_weight and eps are then ignored. */
+#define DIFFATTN_NO_NORM 2u
+
+/*
+ * diffattn_lambda -- Eq. 2: lambda = exp(lq1 . lk1) - exp(lq2 . lk2) + lambda_init.
+ *   lq1, lk1, lq2, lk2 : device fp32 [d], d in 1..4096.
+ *   lambda_out         : device fp32 [1]; written by the kernel.
+ * One scalar per call (per layer); it is shared by all heads and tokens and
+ * is not clamped (it may be negative or exceed 1).
+ */
+DIFFATTN_API diffattn_status diffattn_lambda(const float* lq1, const float* lk1, const float* lq2,
+                                const float* lk2, int d, float lambda_init,
+                                float* lambda_out, void* stream);
+
+/*
+ * diffattn_fwd -- prefill: Eq. 1 for every query row, then Eq. 3.
+ *   q1, k1, q2, k2 : [B, H, N, d]   of dtype dt
+ *   v              : [B, H, N, 2d]  of dtype dt
+ *   out            : [B, H, N, 2d]  of dtype dt (bf16 results are rounded to
+ *                    nearest-even from fp32)
+ *   lambda         : device fp32 [1] (e.g. from diffattn_lambda)
+ *   lambda_init    : host scalar; the output is multiplied by (1 - lambda_init)
+ *   norm_weight    : device fp32 [2d] shared by all heads, or NULL for ones
+ *   eps            : added to mean(Y^2) inside the square root (>= 0)
+ *   flags          : DIFFATTN_CAUSAL | DIFFATTN_NO_NORM
+ * Softmax and all accumulation are fp32; for dt = BF16 the probabilities
+ * enter the PV product rounded to bf16.
+ */
+DIFFATTN_API diffattn_status diffattn_fwd(diffattn_dtype dt, const void* q1, const void* k1, const void* q2,
+                             const void* k2, const void* v, void* out, int B, int H, int N, int d,
+                             const float* lambda, float lambda_init, const float* norm_weight,
+                             float eps, unsigned flags, void* stream);
+
+/*
+ * diffattn_decode_workspace_bytes -- bytes of device scratch that
+ * diffattn_decode needs for these sizes (0 if the sizes are invalid or
+ * empty).  The caller allocates it; its contents need no initialisation.
+ */
+DIFFATTN_API size_t diffattn_decode_workspace_bytes(int B, int H, int L_max, int d);
+
+/*
+ * diffattn_decode -- one new query token per sequence against a KV cache.
+ *   q1, q2    : [B, H, 1, d]
+ *   k1c, k2c  : [B, H, L_max, d]
+ *   vc        : [B, H, L_max, 2d]
+ *   cache_len : device int32 [B]; sequence b attends cached keys
+ *               [0, cache_len[b]) with no mask (the new token's keys are
+ *               already in the cache).  NULL means L_max for all.  Values are
+ *               clamped to [0, L_max]; a sequence with 0 keys outputs zeros.
+ *   out       : [B, H, 1, 2d]
+ *   lambda, lambda_init, norm_weight, eps: as for diffattn_fwd.
+ *   workspace : device scratch of at least
+ *               diffattn_decode_workspace_bytes(B, H, L_max, d) bytes,
+ *               16-byte aligned; calls that share a workspace must be
+ *               ordered on one stream.
+ * The split over the cache is a fixed function of (B, H, L_max, d), and
+ * partial results merge in a fixed order, so results are deterministic.
+ */
+DIFFATTN_API diffattn_status diffattn_decode(diffattn_dtype dt, const void* q1, const void* q2,
+                                const void* k1c, const void* k2c, const void* vc,
+                                const int* cache_len, void* out, int B, int H, int L_max, int d,
+                                const float* lambda, float lambda_init, const float* norm_weight,
+                                float eps, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static English text for a status code (never NULL). */
+DIFFATTN_API const char* diffattn_strerror(diffattn_status status);
+
+/* DIFFATTN_ABI_VERSION of the built library. */
+DIFFATTN_API int diffattn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DIFFATTN_H */

@@ -1,0 +1,130 @@
+"""The C ABI without a GPU: the library loads, exports exactly what
+include/diffattn.h declares, and rejects bad arguments before any HIP call.
+
+Every call below fails validation (or is empty work), so nothing is launched.
+Fake device pointers are plain integers that are never dereferenced.
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from transformer_attention_diffattn_amd import binding as b
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "diffattn.h")
+
+A16 = 0x100000  # a 16-byte aligned fake device address (never dereferenced)
+MIS = 0x100004  # a misaligned one
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"DIFFATTN_API\s+[\w\s\*]*?\b(diffattn_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(b.LIB_PATH):
+        pytest.skip("libdiffattn.so not built")
+    return b.lib()
+
+
+def test_header_declares_the_abi():
+    assert declared_symbols() == sorted([
+        "diffattn_abi_version", "diffattn_decode", "diffattn_decode_workspace_bytes",
+        "diffattn_fwd", "diffattn_lambda", "diffattn_strerror"])
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_symbols():
+        assert hasattr(L, name), name
+    nm = subprocess.run(["nm", "-D", "--defined-only", b.LIB_PATH], capture_output=True, text=True)
+    if nm.returncode == 0:
+        exported = {ln.split()[-1] for ln in nm.stdout.splitlines() if " T " in ln}
+        ours = {s for s in exported if s.startswith("diffattn")}
+        assert ours == set(declared_symbols())
+
+
+def test_version_and_strerror(L):
+    assert L.diffattn_abi_version() == 1
+    for code in range(5):
+        assert L.diffattn_strerror(code)
+    assert L.diffattn_strerror(99) == b"unknown status"
+
+
+def _fwd(L, dt=b.BF16, ptrs=(A16,) * 6, B=1, H=1, N=8, d=64, lam=A16, w=None, eps=1e-5, flags=b.CAUSAL):
+    return L.diffattn_fwd(dt, *ptrs, B, H, N, d, lam, 0.8, w, eps, flags, None)
+
+
+def test_fwd_validation(L):
+    assert _fwd(L, dt=5) == b.EUNSUPPORTED
+    for d in (0, 8, 48, 96, 256):
+        assert _fwd(L, d=d) == b.EUNSUPPORTED
+    assert _fwd(L, B=-1) == b.EINVAL
+    assert _fwd(L, N=-3) == b.EINVAL
+    assert _fwd(L, flags=4) == b.EINVAL
+    assert _fwd(L, eps=-1.0) == b.EINVAL
+    assert _fwd(L, eps=float("nan")) == b.EINVAL
+    for i in range(6):
+        p = [A16] * 6
+        p[i] = None
+        assert _fwd(L, ptrs=p) == b.EINVAL
+        p[i] = MIS
+        assert _fwd(L, ptrs=p) == b.EINVAL
+    assert _fwd(L, lam=None) == b.EINVAL
+    assert _fwd(L, w=A16 + 2) == b.EINVAL
+    # a query grid larger than a launch can hold
+    assert _fwd(L, B=65535, H=65535, N=1 << 20) == b.EINVAL
+
+
+def test_fwd_empty_work_is_ok_without_launch(L):
+    assert _fwd(L, B=0) == b.OK
+    assert _fwd(L, H=0) == b.OK
+    assert _fwd(L, N=0) == b.OK
+    # empty tensors may carry null data pointers
+    assert _fwd(L, N=0, ptrs=(None,) * 6, lam=None) == b.OK
+    assert _fwd(L, N=0, d=48) == b.EUNSUPPORTED
+
+
+def test_lambda_validation(L):
+    assert L.diffattn_lambda(None, A16, A16, A16, 64, 0.8, A16, None) == b.EINVAL
+    assert L.diffattn_lambda(A16, A16, A16, A16, 0, 0.8, A16, None) == b.EINVAL
+    assert L.diffattn_lambda(A16, A16, A16, A16, 5000, 0.8, A16, None) == b.EINVAL
+    assert L.diffattn_lambda(A16, A16, A16, A16, 64, float("inf"), A16, None) == b.EINVAL
+    assert L.diffattn_lambda(A16, A16, A16, A16 + 1, 64, 0.8, A16, None) == b.EINVAL
+
+
+def test_decode_workspace_bytes(L):
+    assert L.diffattn_decode_workspace_bytes(0, 16, 100, 128) == 0
+    assert L.diffattn_decode_workspace_bytes(2, 16, 100, 48) == 0
+    n = L.diffattn_decode_workspace_bytes(64, 16, 32768, 128)
+    rec = (4 + 4 * 128) * 4
+    assert n > 0 and n % (64 * 16 * rec) == 0
+    # an empty cache still needs one record per (b, h) for the zero output
+    assert L.diffattn_decode_workspace_bytes(2, 3, 0, 16) == 2 * 3 * (4 + 64) * 4
+
+
+def _dec(L, dt=b.BF16, d=128, B=2, H=2, Lmax=64, ws=A16, wsb=1 << 20, lens=None, ptrs=(A16,) * 6, eps=1e-5):
+    q1, q2, k1, k2, v, out = ptrs
+    return L.diffattn_decode(dt, q1, q2, k1, k2, v, lens, out, B, H, Lmax, d, A16, 0.8, None, eps, ws, wsb, None)
+
+
+def test_decode_validation(L):
+    assert _dec(L, dt=3) == b.EUNSUPPORTED
+    assert _dec(L, d=100) == b.EUNSUPPORTED
+    assert _dec(L, Lmax=-1) == b.EINVAL
+    assert _dec(L, eps=-1e-3) == b.EINVAL
+    assert _dec(L, ws=None) == b.EWORKSPACE
+    assert _dec(L, wsb=16) == b.EWORKSPACE
+    assert _dec(L, ws=A16 + 8) == b.EINVAL
+    assert _dec(L, lens=A16 + 2) == b.EINVAL
+    for i in range(6):
+        p = [A16] * 6
+        p[i] = MIS
+        assert _dec(L, ptrs=p) == b.EINVAL
+    assert _dec(L, B=0) == b.OK
+    assert _dec(L, B=70000) == b.EINVAL

@@ -1,0 +1,298 @@
+"""GPU parity: the HIP path through the C ABI against the CPU fp64 oracle.
+
+Tolerances (max |gpu - oracle| over every compared element, after the norm
+and the scale): 1e-5 for fp32 inputs, 2e-2 for bf16 inputs.  Small shapes
+are compared in full (several tiles plus a ragged tail); the full-size
+workloads are compared on sampled rows (each with its full causal prefix) and
+sampled (batch, head) decode slices, in the launch configuration the
+benchmark times.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import diffattn_oracle as O
+from transformer_attention_diffattn_amd import binding as da
+from transformer_attention_diffattn_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"fp32": 1e-5, "bf16": 2e-2}
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    return torch.device("cuda:0")
+
+
+def _to(x, dev):
+    return {k: (t.to(dev) if torch.is_tensor(t) else t) for k, t in x.items()}
+
+
+def _lam_host(x):
+    return O.lambda_scalar(x["lq1"], x["lk1"], x["lq2"], x["lk2"], x["lambda_init"])
+
+
+def _gpu_prefill(x, dev, causal=True, norm=True, weight=None, lam_value=None):
+    g = _to(x, dev)
+    if lam_value is None:
+        lam_t = da.lam(g["lq1"], g["lk1"], g["lq2"], g["lk2"], g["lambda_init"])
+    else:
+        lam_t = torch.tensor([lam_value], dtype=torch.float32, device=dev)
+    w = None if weight is None else weight.to(dev)
+    out = da.fwd(g["q1"], g["k1"], g["q2"], g["k2"], g["v"], lam_t, g["lambda_init"], weight=w,
+                 eps=g["eps"], causal=causal, norm=norm)
+    torch.cuda.synchronize()
+    return out
+
+
+def _maxerr(a, b):
+    return float(np.max(np.abs(np.asarray(a, dtype=np.float64) - b))) if np.size(b) else 0.0
+
+
+# ---------------------------------------------------------------------------
+# lambda (Eq. 2)
+
+
+@pytest.mark.parametrize("d", [16, 64, 128])
+def test_lambda_kernel(dev, d):
+    x = W.prefill_inputs(1, 1, 1, d, "fp32", seed=100 + d, lam_std=0.3)
+    g = _to(x, dev)
+    got = da.lam(g["lq1"], g["lk1"], g["lq2"], g["lk2"], g["lambda_init"]).item()
+    ref = _lam_host(x)
+    assert abs(got - ref) <= 1e-6 * max(1.0, abs(ref)), (got, ref)
+
+
+# ---------------------------------------------------------------------------
+# prefill, full comparison on small shapes
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("N", [1, 77, 200, 257])
+def test_prefill_small(dev, dtype, d, causal, N):
+    print(f"case prefill {dtype} d={d} causal={causal} N={N}", flush=True)
+    x = W.prefill_inputs(2, 2, N, d, dtype, seed=1000 + N + d)
+    out = _gpu_prefill(x, dev, causal=causal)
+    ref = O.forward(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], _lam_host(x), x["lambda_init"],
+                    eps=x["eps"], causal=causal)
+    err = _maxerr(out.float().cpu().numpy(), ref)
+    assert err <= TOL[dtype], err
+
+
+def test_config_tiny_fp32(dev):
+    w = W.WORKLOADS["tiny_fp32_b1h1n128d16"]
+    x = W.workload_inputs(w.name)
+    out = _gpu_prefill(x, dev, causal=w.causal)
+    ref = O.forward(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], _lam_host(x), x["lambda_init"],
+                    eps=x["eps"], causal=True)
+    err = _maxerr(out.cpu().numpy(), ref)
+    assert err <= 1e-5, err
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("lam", [-0.3, 0.0, 1.0, 1.7])
+def test_lambda_outside_unit_interval(dev, dtype, lam):
+    x = W.prefill_inputs(1, 3, 150, 64, dtype, seed=31)
+    out = _gpu_prefill(x, dev, lam_value=lam)
+    ref = O.forward(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam, x["lambda_init"], eps=x["eps"])
+    assert _maxerr(out.float().cpu().numpy(), ref) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("lam", [-0.3, 0.5, 1.0, 1.7])
+def test_rows_sum_to_one_minus_lambda(dev, dtype, lam):
+    # V = ones and no norm: Y = sum_j D_ij = 1 - lambda for every row
+    x = W.prefill_inputs(1, 2, 130, 32, dtype, seed=32)
+    x["v"] = torch.ones_like(x["v"])
+    out = _gpu_prefill(x, dev, norm=False, lam_value=lam).float().cpu().numpy()
+    tol = 1e-5 if dtype == "fp32" else 4e-3
+    assert np.max(np.abs(out - (1.0 - lam))) <= tol
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_six_key_example(dev, dtype):
+    # page "Differential attention", section "The noise-canceling idea":
+    # scores [0.5, 3, 0.5 x4] and [0.5 x6], lambda 0.5, printed weights
+    d, n = 16, 6
+    q = torch.zeros(1, 1, n, d)
+    q[..., 0] = 4.0  # q.k / sqrt(16) = k[0]
+    k1 = torch.zeros(1, 1, n, d)
+    k1[0, 0, :, 0] = torch.tensor([0.5, 3.0, 0.5, 0.5, 0.5, 0.5])
+    k2 = torch.zeros(1, 1, n, d)
+    k2[..., 0] = 0.5
+    v = torch.zeros(1, 1, n, 2 * d)
+    v[0, 0, :, :n] = torch.eye(n)
+    dt = W.DTYPES[dtype]
+    x = dict(q1=q.to(dt), k1=k1.to(dt), q2=q.to(dt), k2=k2.to(dt), v=v.to(dt), lambda_init=0.5, eps=1e-5,
+             lq1=torch.zeros(d), lk1=torch.zeros(d), lq2=torch.zeros(d), lk2=torch.zeros(d))
+    out = _gpu_prefill(x, dev, causal=False, norm=False).float().cpu().numpy()[0, 0]
+    printed = np.array([-0.025, 0.626, -0.025, -0.025, -0.025, -0.025])
+    tol = 5e-4 if dtype == "fp32" else 5e-3
+    for row in out:
+        assert np.max(np.abs(row[:n] - printed)) <= tol
+        assert abs(row[[0, 2, 3, 4, 5]].sum() - (-0.126)) <= 2 * tol
+        assert np.all(row[n:] == 0.0)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_shared_maps_and_weight(dev, dtype):
+    x = W.prefill_inputs(2, 2, 190, 64, dtype, seed=33)
+    x["q2"], x["k2"] = x["q1"].clone(), x["k1"].clone()
+    wt = torch.linspace(0.5, 1.5, 128, dtype=torch.float32)
+    out = _gpu_prefill(x, dev, weight=wt)
+    ref = O.forward(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], _lam_host(x), x["lambda_init"],
+                    weight=wt.numpy(), eps=x["eps"])
+    assert _maxerr(out.float().cpu().numpy(), ref) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_large_logits(dev, dtype):
+    # logits of a few hundred (trained top-1 logits of 318 are reported on
+    # the review page, "Strengths"): the running maximum must keep exp finite
+    x = W.prefill_inputs(1, 2, 160, 64, dtype, seed=34, qk_scale=6.0)
+    out = _gpu_prefill(x, dev)
+    q = x["q1"].double()
+    k = x["k1"].double()
+    assert (q @ k.transpose(-1, -2)).abs().max().item() / 8.0 > 100.0
+    o = out.float().cpu().numpy()
+    assert np.all(np.isfinite(o))
+    ref = O.forward(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], _lam_host(x), x["lambda_init"], eps=x["eps"])
+    tol = 1e-4 if dtype == "fp32" else TOL[dtype]
+    assert _maxerr(o, ref) <= tol
+
+
+def test_empty_inputs_are_noops(dev):
+    for shape in ((0, 2, 8, 16), (1, 2, 0, 16)):
+        q = torch.zeros(shape, device=dev, dtype=torch.bfloat16)
+        v = torch.zeros(shape[:3] + (32,), device=dev, dtype=torch.bfloat16)
+        lam_t = torch.zeros(1, device=dev)
+        out = da.fwd(q, q, q, q, v, lam_t, 0.8)
+        torch.cuda.synchronize()
+        assert out.shape == v.shape
+
+
+def test_prefill_deterministic(dev):
+    x = W.prefill_inputs(2, 4, 600, 128, "bf16", seed=35)
+    a = _gpu_prefill(x, dev)
+    b = _gpu_prefill(x, dev)
+    assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# decode
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("d", [16, 64, 128])
+def test_decode_small(dev, dtype, d):
+    print(f"case decode {dtype} d={d}", flush=True)
+    lens = [300, 1, 0, 257, 64]
+    y = W.decode_inputs(5, 3, 300, d, dtype, seed=200 + d, cache_len=lens)
+    g = _to(y, dev)
+    lam_t = da.lam(g["lq1"], g["lk1"], g["lq2"], g["lk2"], g["lambda_init"])
+    out = da.decode(g["q1"], g["q2"], g["k1c"], g["k2c"], g["vc"], lam_t, g["lambda_init"],
+                    cache_len=g["cache_len"], eps=g["eps"])
+    torch.cuda.synchronize()
+    ref = O.decode(y["q1"][:, :, 0], y["q2"][:, :, 0], y["k1c"], y["k2c"], y["vc"], np.array(lens), _lam_host(y),
+                   y["lambda_init"], eps=y["eps"])
+    o = out[:, :, 0].float().cpu().numpy()
+    assert np.all(o[2] == 0.0)  # empty cache -> zeros
+    assert _maxerr(o, ref) <= TOL[dtype]
+
+
+def test_decode_no_cache_len_and_long_cache(dev):
+    y = W.decode_inputs(2, 2, 5000, 128, "bf16", seed=210)
+    g = _to(y, dev)
+    lam_t = da.lam(g["lq1"], g["lk1"], g["lq2"], g["lk2"], g["lambda_init"])
+    out = da.decode(g["q1"], g["q2"], g["k1c"], g["k2c"], g["vc"], lam_t, g["lambda_init"], eps=g["eps"])
+    torch.cuda.synchronize()
+    ref = O.decode(y["q1"][:, :, 0], y["q2"][:, :, 0], y["k1c"], y["k2c"], y["vc"], None, _lam_host(y),
+                   y["lambda_init"], eps=y["eps"])
+    assert _maxerr(out[:, :, 0].float().cpu().numpy(), ref) <= 2e-2
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_decode_equals_last_prefill_row(dev, dtype):
+    x = W.prefill_inputs(2, 2, 333, 64, dtype, seed=36)
+    g = _to(x, dev)
+    pre = _gpu_prefill(x, dev)
+    lam_t = da.lam(g["lq1"], g["lk1"], g["lq2"], g["lk2"], g["lambda_init"])
+    dec = da.decode(g["q1"][:, :, -1:].contiguous(), g["q2"][:, :, -1:].contiguous(), g["k1"], g["k2"], g["v"],
+                    lam_t, g["lambda_init"], eps=g["eps"])
+    torch.cuda.synchronize()
+    diff = (dec[:, :, 0].float() - pre[:, :, -1].float()).abs().max().item()
+    assert diff <= TOL[dtype], diff
+
+
+def test_decode_deterministic(dev):
+    y = W.decode_inputs(4, 4, 3000, 128, "bf16", seed=37, cache_len=[3000, 1234, 77, 2999])
+    g = _to(y, dev)
+    lam_t = da.lam(g["lq1"], g["lk1"], g["lq2"], g["lk2"], g["lambda_init"])
+    args = (g["q1"], g["q2"], g["k1c"], g["k2c"], g["vc"], lam_t, g["lambda_init"])
+    a = da.decode(*args, cache_len=g["cache_len"])
+    b = da.decode(*args, cache_len=g["cache_len"])
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, sampled outputs
+
+
+def _sample_rows(N, rng, extra=()):
+    rows = {0, 1, 15, 16, 63, 64, 127, 128, 129, N // 2, N - 2, N - 1, *extra}
+    rows |= set(rng.integers(0, N, 16).tolist())
+    return np.array(sorted(r for r in rows if 0 <= r < N))
+
+
+@pytest.mark.parametrize("name", ["layer1p4b_bf16_b4h16n2048d64", "layer3b_bf16_b2h12n4096d128",
+                                  "longctx_bf16_b1h12n65536d128"])
+def test_full_size_prefill_sampled(dev, name):
+    w = W.WORKLOADS[name]
+    print(f"case full-size {name}", flush=True)
+    x = W.workload_inputs(name, device=dev)
+    lam_t = da.lam(x["lq1"], x["lk1"], x["lq2"], x["lk2"], x["lambda_init"])
+    out = da.fwd(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam_t, x["lambda_init"], eps=x["eps"],
+                 causal=w.causal)
+    torch.cuda.synchronize()
+    lam = _lam_host({k: (x[k].cpu() if torch.is_tensor(x[k]) else x[k])
+                     for k in ("lq1", "lk1", "lq2", "lk2", "lambda_init")})
+    rng = np.random.default_rng(w.seed)
+    heads = [(0, 0), (w.B - 1, w.H - 1), (w.B // 2, w.H // 2)]
+    needle_rows = tuple(o + 1000 for o in w.needle_offsets) + tuple(w.needle_offsets)
+    worst = 0.0
+    for b, h in heads:
+        rows = _sample_rows(w.N, rng, needle_rows)
+        ref = O.forward_rows(*(x[k][b, h].cpu() for k in ("q1", "k1", "q2", "k2", "v")), rows, lam,
+                             x["lambda_init"], eps=x["eps"], causal=w.causal)
+        got = out[b, h][torch.from_numpy(rows).to(dev)].float().cpu().numpy()
+        assert np.all(np.isfinite(got))
+        worst = max(worst, _maxerr(got, ref))
+    print(f"{name}: sampled max|err| = {worst:.3e}", flush=True)
+    assert worst <= 2e-2
+
+
+def test_full_size_decode_sampled(dev):
+    w = W.WORKLOADS["decode_bf16_b64h16l32768d128"]
+    y = W.workload_inputs(w.name, device=dev)
+    lam_t = da.lam(y["lq1"], y["lk1"], y["lq2"], y["lk2"], y["lambda_init"])
+    out = da.decode(y["q1"], y["q2"], y["k1c"], y["k2c"], y["vc"], lam_t, y["lambda_init"],
+                    cache_len=y["cache_len"], eps=y["eps"])
+    torch.cuda.synchronize()
+    lam = _lam_host({k: (y[k].cpu() if torch.is_tensor(y[k]) else y[k])
+                     for k in ("lq1", "lk1", "lq2", "lk2", "lambda_init")})
+    worst = 0.0
+    for b, h in [(0, 0), (63, 15), (17, 9), (40, 3)]:
+        ref = O.decode(y["q1"][b:b + 1, h:h + 1, 0].cpu(), y["q2"][b:b + 1, h:h + 1, 0].cpu(),
+                       y["k1c"][b:b + 1, h:h + 1].cpu(), y["k2c"][b:b + 1, h:h + 1].cpu(),
+                       y["vc"][b:b + 1, h:h + 1].cpu(), None, lam, y["lambda_init"], eps=y["eps"])
+        got = out[b, h, 0].float().cpu().numpy()
+        worst = max(worst, _maxerr(got, ref[0, 0]))
+    print(f"decode full-size: sampled max|err| = {worst:.3e}", flush=True)
+    assert worst <= 2e-2
+    del y
+    torch.cuda.empty_cache()

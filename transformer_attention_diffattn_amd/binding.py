@@ -1,0 +1,159 @@
+"""ctypes binding of libdiffattn.so (C ABI in include/diffattn.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of the library.  torch supplies device memory and the current stream.
+There is no fallback: if the library is missing or the tensors are not on a
+HIP device, these functions raise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdiffattn.so")
+
+OK, EINVAL, EUNSUPPORTED, EHIP, EWORKSPACE = 0, 1, 2, 3, 4
+FP32, BF16 = 0, 1
+CAUSAL, NO_NORM = 1, 2
+
+_DT = {torch.float32: FP32, torch.bfloat16: BF16}
+_lib = None
+
+vp = ctypes.c_void_p
+
+
+def lib() -> ctypes.CDLL:
+    """Load the library once and declare the C signatures."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build() "
+                               "or python -m transformer_attention_diffattn_amd.build_lib")
+        L = ctypes.CDLL(LIB_PATH)
+        i, f, u, sz = ctypes.c_int, ctypes.c_float, ctypes.c_uint, ctypes.c_size_t
+        L.diffattn_lambda.argtypes = [vp, vp, vp, vp, i, f, vp, vp]
+        L.diffattn_lambda.restype = i
+        L.diffattn_fwd.argtypes = [i, vp, vp, vp, vp, vp, vp, i, i, i, i, vp, f, vp, f, u, vp]
+        L.diffattn_fwd.restype = i
+        L.diffattn_decode_workspace_bytes.argtypes = [i, i, i, i]
+        L.diffattn_decode_workspace_bytes.restype = sz
+        L.diffattn_decode.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, vp, f, vp, f, vp, sz, vp]
+        L.diffattn_decode.restype = i
+        L.diffattn_strerror.argtypes = [i]
+        L.diffattn_strerror.restype = ctypes.c_char_p
+        L.diffattn_abi_version.argtypes = []
+        L.diffattn_abi_version.restype = i
+        _lib = L
+    return _lib
+
+
+def _check(status: int, what: str) -> None:
+    if status != OK:
+        msg = lib().diffattn_strerror(status).decode()
+        raise RuntimeError(f"{what} failed: status {status} ({msg})")
+
+
+def _dev(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a tensor on a HIP device")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def lam(lq1, lk1, lq2, lk2, lambda_init: float, out: torch.Tensor | None = None) -> torch.Tensor:
+    """lambda = exp(lq1.lk1) - exp(lq2.lk2) + lambda_init as a device fp32 [1]."""
+    for n, t in (("lq1", lq1), ("lk1", lk1), ("lq2", lq2), ("lk2", lk2)):
+        _dev(t, n)
+        if t.dtype != torch.float32 or t.dim() != 1 or t.numel() != lq1.numel():
+            raise ValueError(f"{n} must be fp32 [d]")
+    if out is None:
+        out = torch.empty(1, device=lq1.device, dtype=torch.float32)
+    _check(lib().diffattn_lambda(_ptr(lq1), _ptr(lk1), _ptr(lq2), _ptr(lk2), lq1.numel(), float(lambda_init),
+                                 _ptr(out), _stream(lq1.device)), "diffattn_lambda")
+    return out
+
+
+def fwd(q1, k1, q2, k2, v, lam_t, lambda_init: float, weight=None, eps: float = 1e-5,
+        causal: bool = True, norm: bool = True, out=None) -> torch.Tensor:
+    """Differential-attention prefill.  q1/k1/q2/k2 [B,H,N,d], v [B,H,N,2d] ->
+    out [B,H,N,2d] (same dtype).  lam_t: device fp32 [1]."""
+    for n, t in (("q1", q1), ("k1", k1), ("q2", q2), ("k2", k2), ("v", v), ("lambda", lam_t)):
+        _dev(t, n)
+    if q1.dtype not in _DT:
+        raise ValueError("dtype must be float32 or bfloat16")
+    B, H, N, d = q1.shape
+    for n, t in (("k1", k1), ("q2", q2), ("k2", k2)):
+        if t.shape != q1.shape or t.dtype != q1.dtype:
+            raise ValueError(f"{n} must match q1 in shape and dtype")
+    if v.shape != (B, H, N, 2 * d) or v.dtype != q1.dtype:
+        raise ValueError("v must be [B,H,N,2d] of q1's dtype")
+    if lam_t.dtype != torch.float32:
+        raise ValueError("lambda must be fp32")
+    if weight is not None:
+        _dev(weight, "weight")
+        if weight.dtype != torch.float32 or weight.shape != (2 * d,):
+            raise ValueError("weight must be fp32 [2d]")
+    if out is None:
+        out = torch.empty_like(v)
+    else:
+        _dev(out, "out")
+        if out.shape != v.shape or out.dtype != v.dtype:
+            raise ValueError("out must match v")
+    flags = (CAUSAL if causal else 0) | (0 if norm else NO_NORM)
+    _check(lib().diffattn_fwd(_DT[q1.dtype], _ptr(q1), _ptr(k1), _ptr(q2), _ptr(k2), _ptr(v), _ptr(out),
+                              B, H, N, d, _ptr(lam_t), float(lambda_init), _ptr(weight), float(eps), flags,
+                              _stream(q1.device)), "diffattn_fwd")
+    return out
+
+
+def decode_workspace_bytes(B: int, H: int, L: int, d: int) -> int:
+    return int(lib().diffattn_decode_workspace_bytes(B, H, L, d))
+
+
+def decode(q1, q2, k1c, k2c, vc, lam_t, lambda_init: float, cache_len=None, weight=None,
+           eps: float = 1e-5, workspace=None, out=None) -> torch.Tensor:
+    """One decode step.  q1/q2 [B,H,1,d]; caches k1c/k2c [B,H,L,d], vc [B,H,L,2d];
+    cache_len: device int32 [B] or None -> out [B,H,1,2d]."""
+    for n, t in (("q1", q1), ("q2", q2), ("k1c", k1c), ("k2c", k2c), ("vc", vc), ("lambda", lam_t)):
+        _dev(t, n)
+    if q1.dtype not in _DT:
+        raise ValueError("dtype must be float32 or bfloat16")
+    B, H, one, d = q1.shape
+    L = k1c.shape[2]
+    if one != 1 or q2.shape != q1.shape:
+        raise ValueError("q1/q2 must be [B,H,1,d]")
+    if k1c.shape != (B, H, L, d) or k2c.shape != (B, H, L, d) or vc.shape != (B, H, L, 2 * d):
+        raise ValueError("caches must be [B,H,L,d] and [B,H,L,2d]")
+    for t in (q2, k1c, k2c, vc):
+        if t.dtype != q1.dtype:
+            raise ValueError("all of q/k/v must share one dtype")
+    if cache_len is not None:
+        _dev(cache_len, "cache_len")
+        if cache_len.dtype != torch.int32 or cache_len.shape != (B,):
+            raise ValueError("cache_len must be int32 [B]")
+    if weight is not None:
+        _dev(weight, "weight")
+        if weight.dtype != torch.float32 or weight.shape != (2 * d,):
+            raise ValueError("weight must be fp32 [2d]")
+    need = decode_workspace_bytes(B, H, L, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q1.device)
+    if out is None:
+        out = torch.empty((B, H, 1, 2 * d), dtype=q1.dtype, device=q1.device)
+    _check(lib().diffattn_decode(_DT[q1.dtype], _ptr(q1), _ptr(q2), _ptr(k1c), _ptr(k2c), _ptr(vc),
+                                 _ptr(cache_len), _ptr(out), B, H, L, d, _ptr(lam_t), float(lambda_init),
+                                 _ptr(weight), float(eps), _ptr(workspace), workspace.numel(),
+                                 _stream(q1.device)), "diffattn_decode")
+    return out

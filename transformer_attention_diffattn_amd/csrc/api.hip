@@ -1,0 +1,164 @@
+// C ABI of libdiffattn.so (declared in include/diffattn.h): argument
+// validation, dispatch and launch.  Validation happens before any HIP call;
+// the library allocates nothing and holds no state.
+
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/diffattn.h"
+#include "device_common.h"
+#include "kernels.h"
+
+namespace diffattn {
+
+// lambda = exp(lq1 . lk1) - exp(lq2 . lk2) + lambda_init   (Eq. 2 of the
+// "Differential Transformer" sample review, "Summary"; the same formula in
+// "Cancelling Context Noise Through Attention Map Subtraction").  One wave.
+__global__ __launch_bounds__(64) void lambda_kernel(const float* __restrict__ lq1, const float* __restrict__ lk1,
+                                                    const float* __restrict__ lq2, const float* __restrict__ lk2,
+                                                    int d, float lambda_init, float* __restrict__ out) {
+  float a = 0.f, b = 0.f;
+  for (int i = threadIdx.x; i < d; i += 64) {
+    a += lq1[i] * lk1[i];
+    b += lq2[i] * lk2[i];
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    a += __shfl_xor(a, off);
+    b += __shfl_xor(b, off);
+  }
+  if (threadIdx.x == 0) out[0] = expf(a) - expf(b) + lambda_init;
+}
+
+hipError_t launch_lambda(const float* lq1, const float* lk1, const float* lq2, const float* lk2, int d,
+                         float lambda_init, float* out, hipStream_t stream) {
+  hipLaunchKernelGGL(lambda_kernel, dim3(1), dim3(64), 0, stream, lq1, lk1, lq2, lk2, d, lambda_init, out);
+  return hipGetLastError();
+}
+
+}  // namespace diffattn
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+bool ok_ptr16(const void* p) { return p != nullptr && aligned(p, 16); }
+bool ok_ptr4(const void* p) { return p != nullptr && aligned(p, 4); }
+bool supported_d(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool finite_nonneg(float x) { return isfinite(x) && x >= 0.f; }
+
+}  // namespace
+
+extern "C" {
+
+int diffattn_abi_version(void) { return DIFFATTN_ABI_VERSION; }
+
+const char* diffattn_strerror(diffattn_status s) {
+  switch (s) {
+    case DIFFATTN_OK: return "ok";
+    case DIFFATTN_EINVAL: return "invalid argument (null or misaligned pointer, negative size, bad flag or eps)";
+    case DIFFATTN_EUNSUPPORTED: return "unsupported dtype or head width d (d must be 16, 32, 64 or 128)";
+    case DIFFATTN_EHIP: return "HIP launch or runtime error";
+    case DIFFATTN_EWORKSPACE: return "decode workspace missing or smaller than diffattn_decode_workspace_bytes()";
+    default: return "unknown status";
+  }
+}
+
+diffattn_status diffattn_lambda(const float* lq1, const float* lk1, const float* lq2, const float* lk2, int d,
+                                float lambda_init, float* lambda_out, void* stream) {
+  if (!ok_ptr4(lq1) || !ok_ptr4(lk1) || !ok_ptr4(lq2) || !ok_ptr4(lk2) || !ok_ptr4(lambda_out))
+    return DIFFATTN_EINVAL;
+  if (d < 1 || d > 4096 || !isfinite(lambda_init)) return DIFFATTN_EINVAL;
+  hipError_t e = diffattn::launch_lambda(lq1, lk1, lq2, lk2, d, lambda_init, lambda_out, (hipStream_t)stream);
+  return e == hipSuccess ? DIFFATTN_OK : DIFFATTN_EHIP;
+}
+
+diffattn_status diffattn_fwd(diffattn_dtype dt, const void* q1, const void* k1, const void* q2, const void* k2,
+                             const void* v, void* out, int B, int H, int N, int d, const float* lambda,
+                             float lambda_init, const float* norm_weight, float eps, unsigned flags,
+                             void* stream) {
+  if (dt != DIFFATTN_FP32 && dt != DIFFATTN_BF16) return DIFFATTN_EUNSUPPORTED;
+  if (!supported_d(d)) return DIFFATTN_EUNSUPPORTED;
+  if (B < 0 || H < 0 || N < 0) return DIFFATTN_EINVAL;
+  if (flags & ~(DIFFATTN_CAUSAL | DIFFATTN_NO_NORM)) return DIFFATTN_EINVAL;
+  const bool norm = !(flags & DIFFATTN_NO_NORM);
+  if (norm && (!finite_nonneg(eps) || !isfinite(lambda_init))) return DIFFATTN_EINVAL;
+  if ((long long)B * H * N == 0) return DIFFATTN_OK;  // empty work: pointers are not inspected
+  if (!ok_ptr16(q1) || !ok_ptr16(k1) || !ok_ptr16(q2) || !ok_ptr16(k2) || !ok_ptr16(v) || !ok_ptr16(out))
+    return DIFFATTN_EINVAL;
+  if (!ok_ptr4(lambda)) return DIFFATTN_EINVAL;
+  if (norm_weight && !aligned(norm_weight, 4)) return DIFFATTN_EINVAL;
+  const long long BH = (long long)B * H;
+  const bool bf16 = dt == DIFFATTN_BF16;
+  const int bm = diffattn::prefill_block_rows(bf16);
+  const long long qtiles = ((long long)N + bm - 1) / bm;
+  // one workgroup per (query tile, head); a launch holds at most 2^32 - 1 work-items
+  if (BH > INT32_MAX || qtiles * BH * diffattn::prefill_block_threads(bf16) > (long long)UINT32_MAX)
+    return DIFFATTN_EINVAL;
+
+  diffattn::PrefillArgs a;
+  a.q1 = q1;
+  a.k1 = k1;
+  a.q2 = q2;
+  a.k2 = k2;
+  a.v = v;
+  a.out = out;
+  a.BH = (int)BH;
+  a.N = N;
+  a.n_qtiles = (int)qtiles;
+  a.lambda = lambda;
+  a.out_scale = 1.0f - lambda_init;
+  a.norm_w = norm_weight;
+  a.eps = eps;
+  a.c = (float)(1.4426950408889634 / sqrt((double)d));
+  hipError_t e = diffattn::launch_prefill(bf16, d, (flags & DIFFATTN_CAUSAL) != 0, norm, a, (hipStream_t)stream);
+  return e == hipSuccess ? DIFFATTN_OK : DIFFATTN_EHIP;
+}
+
+size_t diffattn_decode_workspace_bytes(int B, int H, int L_max, int d) {
+  if (B <= 0 || H <= 0 || L_max < 0 || !supported_d(d)) return 0;
+  int S = 1, chunk = 0;
+  diffattn::decode_plan(B, H, L_max, d, &S, &chunk);
+  return (size_t)B * H * S * diffattn::decode_record_floats(d) * sizeof(float);
+}
+
+diffattn_status diffattn_decode(diffattn_dtype dt, const void* q1, const void* q2, const void* k1c, const void* k2c,
+                                const void* vc, const int* cache_len, void* out, int B, int H, int L_max, int d,
+                                const float* lambda, float lambda_init, const float* norm_weight, float eps,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (dt != DIFFATTN_FP32 && dt != DIFFATTN_BF16) return DIFFATTN_EUNSUPPORTED;
+  if (!supported_d(d)) return DIFFATTN_EUNSUPPORTED;
+  if (B < 0 || H < 0 || L_max < 0) return DIFFATTN_EINVAL;
+  if (!finite_nonneg(eps) || !isfinite(lambda_init)) return DIFFATTN_EINVAL;
+  if ((long long)B * H == 0) return DIFFATTN_OK;  // empty work: pointers are not inspected
+  if (B > 65535 || H > 65535) return DIFFATTN_EINVAL;
+  if (!ok_ptr16(q1) || !ok_ptr16(q2) || !ok_ptr16(out) || !ok_ptr4(lambda)) return DIFFATTN_EINVAL;
+  if (L_max > 0 && (!ok_ptr16(k1c) || !ok_ptr16(k2c) || !ok_ptr16(vc))) return DIFFATTN_EINVAL;
+  if (cache_len && !aligned(cache_len, 4)) return DIFFATTN_EINVAL;
+  if (norm_weight && !aligned(norm_weight, 4)) return DIFFATTN_EINVAL;
+  const size_t need = diffattn_decode_workspace_bytes(B, H, L_max, d);
+  if (workspace == nullptr || workspace_bytes < need) return DIFFATTN_EWORKSPACE;
+  if (!aligned(workspace, 16)) return DIFFATTN_EINVAL;
+
+  diffattn::DecodeArgs a;
+  a.q1 = q1;
+  a.q2 = q2;
+  a.k1c = k1c;
+  a.k2c = k2c;
+  a.vc = vc;
+  a.cache_len = cache_len;
+  a.out = out;
+  a.B = B;
+  a.H = H;
+  a.L = L_max;
+  diffattn::decode_plan(B, H, L_max, d, &a.S, &a.chunk);
+  a.lambda = lambda;
+  a.out_scale = 1.0f - lambda_init;
+  a.norm_w = norm_weight;
+  a.eps = eps;
+  a.c = (float)(1.4426950408889634 / sqrt((double)d));
+  a.ws = (float*)workspace;
+  hipError_t e = diffattn::launch_decode(dt == DIFFATTN_BF16, d, true, a, (hipStream_t)stream);
+  return e == hipSuccess ? DIFFATTN_OK : DIFFATTN_EHIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,83 @@
+// Device helpers shared by the differential-attention kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace diffattn {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+// log2(e): softmax weights are formed as 2^(s * log2(e)/sqrt(d) - m) so that
+// one FMA and one v_exp_f32 give exp((s - m')/sqrt(d)).
+constexpr float kLog2e = 1.44269504088896340736f;
+
+// Rescale threshold (log2 units): the running reference maximum of a row is
+// raised only when a new score exceeds it by more than this, so weights stay
+// below 2^8 = 256 -- harmless in fp32 accumulators and in bf16 -- and the
+// accumulators are rescaled only when a row's maximum jumps.  Exact: the
+// numerator and denominator always share the same reference.
+constexpr float kRescaleThreshold = 8.0f;
+
+__device__ __forceinline__ f32x4 mfma16x16x32_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma16x16x4_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Two floats -> two bf16 (round to nearest even, v_cvt_pk_bf16_f32), lo first.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// Reinterpret one 32-bit word.  Always pass a scalar copy: bit-casting a
+// vector element expression (v[i]) directly reads element 0 with this
+// compiler, so vector elements go through these by-value helpers.
+__device__ __forceinline__ float u32_as_f32(uint32_t w) { return __builtin_bit_cast(float, w); }
+__device__ __forceinline__ bf16x2 u32_as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2, w); }
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ u32x4 zero_u32x4() {
+  u32x4 z = {0u, 0u, 0u, 0u};
+  return z;
+}
+
+__device__ __forceinline__ f32x4 zero_f32x4() {
+  f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  return z;
+}
+
+// 16-byte global load / store through plain pointers.
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// Reductions across the four 16-lane groups of a wave (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float max_over_lane_groups(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+
+__device__ __forceinline__ float sum_over_lane_groups(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+__device__ __forceinline__ bool wave_any(bool p) { return __ballot(p) != 0ull; }
+
+}  // namespace diffattn

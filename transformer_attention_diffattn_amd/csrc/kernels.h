@@ -1,0 +1,61 @@
+// Internal launch interface between the C ABI (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace diffattn {
+
+struct PrefillArgs {
+  const void* q1;
+  const void* k1;
+  const void* q2;
+  const void* k2;
+  const void* v;
+  void* out;
+  int BH;         // batch * heads
+  int N;          // sequence length (>= 1)
+  int n_qtiles;   // query tiles per head
+  const float* lambda;  // device scalar
+  float out_scale;      // 1 - lambda_init
+  const float* norm_w;  // device [2d] or null (ones)
+  float eps;
+  float c;              // log2(e) / sqrt(d)
+};
+
+struct DecodeArgs {
+  const void* q1;
+  const void* q2;
+  const void* k1c;
+  const void* k2c;
+  const void* vc;
+  const int* cache_len;  // device [B] or null
+  void* out;
+  int B, H, L;           // L = L_max (>= 0)
+  int S;                 // splits per (b, h)
+  int chunk;             // keys per split
+  const float* lambda;
+  float out_scale;
+  const float* norm_w;
+  float eps;
+  float c;
+  float* ws;             // [B*H*S] records of (4 + 4d) floats
+};
+
+// Query rows and threads per workgroup of the prefill kernels.
+int prefill_block_rows(bool bf16);
+int prefill_block_threads(bool bf16);
+
+hipError_t launch_lambda(const float* lq1, const float* lk1, const float* lq2, const float* lk2,
+                         int d, float lambda_init, float* out, hipStream_t stream);
+
+hipError_t launch_prefill(bool bf16, int d, bool causal, bool norm, const PrefillArgs& a,
+                          hipStream_t stream);
+
+// Split plan for decode: number of splits and keys per split.
+void decode_plan(int B, int H, int L, int d, int* S, int* chunk);
+size_t decode_record_floats(int d);
+
+hipError_t launch_decode(bool bf16, int d, bool norm, const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace diffattn
