@@ -87,203 +87,333 @@ __device__ __forceinline__ void epilogue_values(const f32x4 (&O1)[CB], const f32
 
 // ---------------------------------------------------------------------------
 // bf16 kernel
+//
+// A workgroup owns BM = 128 query rows of one head and runs 8 waves: wave w
+// computes map (w & 1) for the 32 rows of row group (w >> 1), as two 16-row
+// sub-tiles so that each K or V fragment read from LDS feeds two MFMAs.  The
+// two maps of a row group only meet in the epilogue, where the map-2 wave
+// hands O2/l2 to the map-1 wave through LDS.  K1, K2 and V tiles of BN keys
+// arrive by direct global->LDS loads into two stage buffers (the next tile
+// loads while the current one is consumed).  Rows are XOR-swizzled in 16-byte
+// chunks so that fragment reads are free of bank conflicts; V stays row-major
+// and its transposed fragments come from the transposing LDS read
+// (ds_read_b64_tr_b16).
+
+template <int D>
+struct Bf16Tile {
+  static constexpr int DV = 2 * D;
+  static constexpr int WAVES = 8;           // 4 row groups x 2 maps
+  static constexpr int SUB = 2;             // 16-row sub-tiles per wave
+  static constexpr int BM = 16 * SUB * (WAVES / 2);
+  static constexpr int BN = D >= 128 ? 32 : 64;  // d = 128: keeps a wave within 256 registers
+  static constexpr int KS = (D + 31) / 32;  // 32-wide k-steps of the QK^T MFMA
+  static constexpr int NB = BN / 16;        // 16-key score blocks per tile
+  static constexpr int NC = BN / 32;        // 32-key PV k-steps per tile
+  static constexpr int CB = DV / 16;        // 16-channel output blocks
+  static constexpr int NCH = D / 8;         // 16-byte chunks per K row
+  static constexpr int NCV = DV / 8;        // 16-byte chunks per V row
+  static constexpr int RPK = NCH >= 16 ? 1 : 16 / NCH;  // K rows per 256 bytes
+  static constexpr int KSEG = BN * NCH / 64;            // 1 KB segments per K tile
+  static constexpr int VSEG = BN * NCV / 64;
+  static constexpr int NSEG = 2 * KSEG + VSEG;
+  static constexpr int KTILE = BN * D;  // elements
+  static constexpr int VTILE = BN * DV;
+  static constexpr int STAGE = 2 * KTILE + VTILE;
+  static_assert(NSEG % WAVES == 0, "segments split evenly over the waves");
+  // The epilogue exchange (fp32 O2/l2, 16*SUB*DV floats per row group)
+  // reuses both stage buffers, XG row groups at a time.
+  static constexpr int XG_FIT = (2 * STAGE * 2) / (16 * SUB * DV * 4);
+  static constexpr int XG = XG_FIT >= WAVES / 2 ? WAVES / 2 : XG_FIT;
+  static_assert(XG >= 1 && (WAVES / 2) % XG == 0, "exchange phases");
+
+  // physical 16-byte chunk of logical chunk c in K row r
+  static __device__ __forceinline__ int kchunk(int r, int c) { return c ^ ((r / RPK) % NCH); }
+  // physical 16-byte chunk of logical chunk c in V row r: the four rows of a
+  // transposed read land on distinct banks
+  static __device__ __forceinline__ int vchunk(int r, int c) {
+    return (DV * 2 >= 128) ? (c ^ (2 * (r & 3))) : (c ^ (2 * ((r >> 1) & 1)));
+  }
+};
+
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+#define DIFFATTN_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+  s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// max over lanes l, l^16, l^32, l^48 without LDS traffic (v_permlane*_swap)
+__device__ __forceinline__ float max4_groups(float x) {
+  const uint32_t xb = __builtin_bit_cast(uint32_t, x);
+  auto r = __builtin_amdgcn_permlane32_swap(xb, xb, false, false);
+  x = fmaxf(u32_as_f32(r[0]), u32_as_f32(r[1]));
+  const uint32_t yb = __builtin_bit_cast(uint32_t, x);
+  auto q = __builtin_amdgcn_permlane16_swap(yb, yb, false, false);
+  return fmaxf(u32_as_f32(q[0]), u32_as_f32(q[1]));
+}
+
+// One map, one sub-tile: raw scores s (masked ones -inf) -> weights
+// 2^(s c - m) in place, with the threshold rescale of l and O.
+template <int NT, int CB>
+__device__ __forceinline__ void softmax_raw(float (&s)[NT], float c, float& m, f32x4& l, f32x4 (&O)[CB]) {
+  float mt = s[0];
+#pragma unroll
+  for (int i = 1; i < NT; ++i) mt = fmaxf(mt, s[i]);
+  mt = max4_groups(mt) * c;
+  if (wave_any(mt > m + kRescaleThreshold)) {
+    const float mn = fmaxf(m, mt);
+    const float alpha = (mn == -INFINITY) ? 1.0f : exp2_fast(m - mn);
+    m = mn;
+    l *= alpha;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) O[cb] *= alpha;
+  }
+  const float nm = -m;
+#pragma unroll
+  for (int i = 0; i < NT; ++i) s[i] = exp2_fast(__builtin_fmaf(s[i], c, nm));
+}
 
 template <int D, bool CAUSAL, bool NORM>
 __global__ __launch_bounds__(512) void prefill_bf16_kernel(PrefillArgs a) {
-  constexpr int DV = 2 * D;
-  constexpr int WAVES = 8;
-  constexpr int BM = 16 * WAVES;
-  constexpr int BN = (D >= 128) ? 32 : 64;
-  constexpr int KS = (D + 31) / 32;  // 32-wide k-steps of the QK^T MFMA
-  constexpr int NB = BN / 16;        // 16-key score blocks per tile
-  constexpr int NC = BN / 32;        // 32-key chunks per tile (PV k-steps)
-  constexpr int CB = DV / 16;        // 16-channel output blocks
-  constexpr int KP = D + 8;          // K tile row pitch (elements); rows stay 16-byte aligned
-  constexpr int VP = BN + 8;         // V^T tile row pitch (elements)
-  constexpr int KTILE = BN * KP;
-  constexpr int VTILE = DV * VP;
-  constexpr int STAGE = 2 * KTILE + VTILE;
-  constexpr int KCH = BN * D / 8;              // 16-byte chunks per K tile
-  constexpr int VITEMS = (BN / 2) * (DV / 8);  // (key pair, 8-channel chunk) items per V tile
-  static_assert(KCH <= 64 * WAVES && VITEMS <= 64 * WAVES, "one staging item per thread");
+  using T = Bf16Tile<D>;
+  constexpr int DV = T::DV, BN = T::BN, KS = T::KS, NB = T::NB, NC = T::NC, CB = T::CB, SUB = T::SUB;
+  constexpr int NCH = T::NCH, NCV = T::NCV, KSEG = T::KSEG, KTILE = T::KTILE;
 
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t stage0[T::STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t stage1[T::STAGE];
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int lr = lane & 15;  // query (MFMA column) owned by this lane
-  const int lg = lane >> 4;  // lane group: selects rows 4*lg..4*lg+3 of each block
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int mp = wave & 1;   // which map this wave computes
+  const int rg = wave >> 1;  // row group
+  const int lr = lane & 15;  // query column of the 16x16 blocks owned by this lane
+  const int lg = lane >> 4;  // lane group: rows 4*lg..4*lg+3 of each block
   const int N = a.N;
 
-  // Longest tiles first under the causal mask; heads vary fastest.
+  // longest query tiles first under the causal mask; heads vary fastest
   const int bid = blockIdx.x;
   const int bh = bid % a.BH;
   const int qt = CAUSAL ? (a.n_qtiles - 1 - bid / a.BH) : (bid / a.BH);
-  const int q0 = qt * BM;
-  const int qw0 = q0 + 16 * wave;
+  const int q0 = qt * T::BM;
+  const int qw0 = q0 + 16 * SUB * rg;
 
   const size_t hrow = (size_t)bh * (size_t)N;
-  const uint16_t* __restrict__ Q1 = (const uint16_t*)a.q1 + hrow * D;
-  const uint16_t* __restrict__ Q2 = (const uint16_t*)a.q2 + hrow * D;
+  const uint16_t* __restrict__ Qm = (const uint16_t*)(mp ? a.q2 : a.q1) + hrow * D;
   const uint16_t* __restrict__ K1 = (const uint16_t*)a.k1 + hrow * D;
   const uint16_t* __restrict__ K2 = (const uint16_t*)a.k2 + hrow * D;
   const uint16_t* __restrict__ V = (const uint16_t*)a.v + hrow * DV;
 
-  // Q^T fragments: lane holds dims 32ks+8lg..+7 of its query row (zeros past d).
-  bf16x8 qf1[KS], qf2[KS];
-  {
-    const int qrow = min(qw0 + lr, N - 1);
+  // Q^T fragments (B operand of S^T = K Q^T): dims 32ks+8lg..+7 of the row
+  bf16x8 qf[SUB][KS];
+#pragma unroll
+  for (int u = 0; u < SUB; ++u) {
+    const int qrow = min(qw0 + 16 * u + lr, N - 1);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int dc = 32 * ks + 8 * lg;
-      qf1[ks] = as_bf16x8(dc < D ? ld16(Q1 + (size_t)qrow * D + dc) : zero_u32x4());
-      qf2[ks] = as_bf16x8(dc < D ? ld16(Q2 + (size_t)qrow * D + dc) : zero_u32x4());
+      qf[u][ks] = as_bf16x8(dc < D ? ld16(Qm + (size_t)qrow * D + dc) : zero_u32x4());
     }
   }
 
-  const int kend = CAUSAL ? min(N, q0 + BM) : N;
+  const int kend = CAUSAL ? min(N, q0 + T::BM) : N;
   const int nkt = (kend + BN - 1) / BN;
 
-  // staging registers: one K1 chunk, one K2 chunk, one V key pair per thread
-  u32x4 rk1 = zero_u32x4(), rk2 = zero_u32x4(), rva = zero_u32x4(), rvb = zero_u32x4();
-  const int k_row = tid / (D / 8), k_ch = tid % (D / 8);
-  const int v_kp = tid % (BN / 2), v_ch = tid / (BN / 2);
-
-  auto load_tile = [&](int kt) {
+  // Direct global->LDS loads of one key tile: each instruction moves 1 KB
+  // (64 lanes x 16 B) to consecutive LDS; a lane fetches the global chunk
+  // that the swizzle assigns to its LDS position.
+  auto issue_tile = [&](uint16_t* dst, int kt) {
     const int kb = kt * BN;
-    if (tid < KCH) {
-      const int r = min(kb + k_row, N - 1);
-      rk1 = ld16(K1 + (size_t)r * D + 8 * k_ch);
-      rk2 = ld16(K2 + (size_t)r * D + 8 * k_ch);
-    }
-    if (tid < VITEMS) {
-      const int r0 = min(kb + 2 * v_kp, N - 1);
-      const int r1 = min(kb + 2 * v_kp + 1, N - 1);
-      rva = ld16(V + (size_t)r0 * DV + 8 * v_ch);
-      rvb = ld16(V + (size_t)r1 * DV + 8 * v_ch);
-    }
-  };
-  auto store_tile = [&](int buf) {
-    uint16_t* Ks1 = lds + buf * STAGE;
-    uint16_t* Ks2 = Ks1 + KTILE;
-    uint16_t* Vt = Ks1 + 2 * KTILE;
-    if (tid < KCH) {
-      st16(Ks1 + k_row * KP + 8 * k_ch, rk1);
-      st16(Ks2 + k_row * KP + 8 * k_ch, rk2);
-    }
-    if (tid < VITEMS) {
-      // transpose a 2-key x 8-channel block: channel e of keys (2kp, 2kp+1)
-      // becomes one dword of V^T row (8ch+e)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t x = rva[e >> 1], y = rvb[e >> 1];
-        const uint32_t wd = (e & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
-        *reinterpret_cast<uint32_t*>(Vt + (8 * v_ch + e) * VP + 2 * v_kp) = wd;
+    for (int i = 0; i < T::NSEG / T::WAVES; ++i) {
+      const int seg = wave + i * T::WAVES;
+      const uint16_t* src;
+      uint16_t* ldst;
+      if (seg < 2 * KSEG) {
+        const int mtx = seg / KSEG, sg = seg % KSEG;
+        const int r = sg * (64 / NCH) + lane / NCH;
+        const int c = T::kchunk(r, lane % NCH);
+        src = (mtx ? K2 : K1) + (size_t)min(kb + r, N - 1) * D + 8 * c;
+        ldst = dst + mtx * KTILE + sg * 512;
+      } else {
+        const int sg = seg - 2 * KSEG;
+        const int r = sg * (64 / NCV) + lane / NCV;
+        const int c = T::vchunk(r, lane % NCV);
+        src = V + (size_t)min(kb + r, N - 1) * DV + 8 * c;
+        ldst = dst + 2 * KTILE + sg * 512;
       }
+      __builtin_amdgcn_global_load_lds(src, DIFFATTN_LDS(ldst), 16, 0, 0);
     }
   };
 
-  // accumulators
-  f32x4 O1[CB], O2[CB];
+  f32x4 O[SUB][CB], L[SUB];
+  float m[SUB];
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb) {
-    O1[cb] = zero_f32x4();
-    O2[cb] = zero_f32x4();
+  for (int u = 0; u < SUB; ++u) {
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) O[u][cb] = zero_f32x4();
+    L[u] = zero_f32x4();
+    m[u] = -INFINITY;
   }
-  f32x4 L1 = zero_f32x4(), L2 = zero_f32x4();
-  float m1 = -INFINITY, m2 = -INFINITY;
   const float c = a.c;
-  u32x4 ones_u = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+  const u32x4 ones_u = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
   const bf16x8 ones = as_bf16x8(ones_u);
-  const int qabs = qw0 + lr;
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int buf = kt & 1;
-    const bool has_next = kt + 1 < nkt;
-    if (has_next) load_tile(kt + 1);
+  auto compute_tile = [&](const uint16_t* stg, int kt) {
     const int kb = kt * BN;
-    const bool active = (qw0 < N) && (!CAUSAL || kb <= qw0 + 15);
-    if (active) {
-      const uint16_t* Ks1 = lds + buf * STAGE;
-      const uint16_t* Ks2 = Ks1 + KTILE;
-      const uint16_t* Vt = Ks1 + 2 * KTILE;
-      const bool need_mask = (CAUSAL && kb + BN - 1 > qw0) || (kb + BN > N);
+    if (qw0 >= N || (CAUSAL && kb > qw0 + 16 * SUB - 1)) return;  // nothing visible for this wave
+    const bool need_mask = (CAUSAL && kb + BN - 1 > qw0) || (kb + BN > N);
+    const uint16_t* ks_ = stg + mp * KTILE;
+    const uint16_t* vs = stg + 2 * KTILE;
 
-      // scores S^T for both maps; block b covers keys 32(b/2) + {8q + 4(b%2) + j}
-      float t1[4 * NB], t2[4 * NB];
+    // S^T = K Q^T for both sub-tiles; block b holds keys 16b+4lg+j
+    float s[SUB][4 * NB];
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const int krow = 32 * (b >> 1) + 8 * (lr >> 2) + 4 * (b & 1) + (lr & 3);
-        f32x4 s1 = zero_f32x4(), s2 = zero_f32x4();
+    for (int b = 0; b < NB; ++b) {
+      const int kr = 16 * b + lr;
+      f32x4 acc[SUB];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int dc = 32 * ks + 8 * lg;
-          const bf16x8 ka1 = as_bf16x8(dc < D ? ld16(Ks1 + krow * KP + dc) : zero_u32x4());
-          const bf16x8 ka2 = as_bf16x8(dc < D ? ld16(Ks2 + krow * KP + dc) : zero_u32x4());
-          s1 = mfma16x16x32_bf16(ka1, qf1[ks], s1);
-          s2 = mfma16x16x32_bf16(ka2, qf2[ks], s2);
-        }
+      for (int u = 0; u < SUB; ++u) acc[u] = zero_f32x4();
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int ch = 4 * ks + lg;
+        const bf16x8 ka = as_bf16x8(ch < NCH ? ld16(ks_ + kr * D + 8 * T::kchunk(kr, ch)) : zero_u32x4());
+#pragma unroll
+        for (int u = 0; u < SUB; ++u) acc[u] = mfma16x16x32_bf16(ka, qf[u][ks], acc[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < SUB; ++u)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          float x1 = s1[j] * c, x2 = s2[j] * c;
+          float x = acc[u][j];
           if (need_mask) {
-            const int kabs = kb + 32 * (b >> 1) + 8 * lg + 4 * (b & 1) + j;
-            const bool ok = (kabs < N) && (!CAUSAL || kabs <= qabs);
-            x1 = ok ? x1 : -INFINITY;
-            x2 = ok ? x2 : -INFINITY;
+            const int kabs = kb + 16 * b + 4 * lg + j;
+            const int qabs = qw0 + 16 * u + lr;
+            x = ((kabs < N) && (!CAUSAL || kabs <= qabs)) ? x : -INFINITY;
           }
-          t1[4 * b + j] = x1;
-          t2[4 * b + j] = x2;
+          s[u][4 * b + j] = x;
         }
-      }
+    }
 
-      softmax_step<4 * NB, CB>(t1, m1, L1, O1);
-      softmax_step<4 * NB, CB>(t2, m2, L2, O2);
-
-      // P^T fragments: chunk cc takes blocks 2cc (keys 8q+0..3) and 2cc+1 (keys 8q+4..7)
 #pragma unroll
-      for (int cc = 0; cc < NC; ++cc) {
-        u32x4 p1u, p2u;
+    for (int u = 0; u < SUB; ++u) softmax_raw<4 * NB, CB>(s[u], c, m[u], L[u], O[u]);
+
+    // O^T += V^T P^T: P^T fragment of chunk cc = blocks 2cc (e 0..3) and 2cc+1 (e 4..7)
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+      bf16x8 pf[SUB];
+#pragma unroll
+      for (int u = 0; u < SUB; ++u) {
+        u32x4 pu;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const int b = 2 * cc + h;
-          p1u[2 * h] = pack_bf16x2(t1[4 * b + 0], t1[4 * b + 1]);
-          p1u[2 * h + 1] = pack_bf16x2(t1[4 * b + 2], t1[4 * b + 3]);
-          p2u[2 * h] = pack_bf16x2(t2[4 * b + 0], t2[4 * b + 1]);
-          p2u[2 * h + 1] = pack_bf16x2(t2[4 * b + 2], t2[4 * b + 3]);
+          const float* sp = &s[u][4 * (2 * cc + h)];
+          pu[2 * h] = pack_bf16x2(sp[0], sp[1]);
+          pu[2 * h + 1] = pack_bf16x2(sp[2], sp[3]);
         }
-        const bf16x8 p1 = as_bf16x8(p1u), p2 = as_bf16x8(p2u);
-        L1 = mfma16x16x32_bf16(ones, p1, L1);
-        L2 = mfma16x16x32_bf16(ones, p2, L2);
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-          const bf16x8 va = as_bf16x8(ld16(Vt + (16 * cb + lr) * VP + 32 * cc + 8 * lg));
-          O1[cb] = mfma16x16x32_bf16(va, p1, O1[cb]);
-          O2[cb] = mfma16x16x32_bf16(va, p2, O2[cb]);
-        }
+        pf[u] = as_bf16x8(pu);
+        L[u] = mfma16x16x32_bf16(ones, pf[u], L[u]);
       }
-    }
-    if (has_next) store_tile(buf ^ 1);
-    __syncthreads();
-  }
-
-  if (qw0 < N) {
-    f32x4 y[CB];
-    epilogue_values<CB, NORM>(O1, O2, L1[0], L2[0], *a.lambda, a.out_scale, a.eps, a.norm_w, lg, y);
-    const int row = qw0 + lr;
-    if (row < N) {
-      uint16_t* __restrict__ Out = (uint16_t*)a.out + (hrow + row) * DV;
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
-        u32x2 pk = {pack_bf16x2(y[cb][0], y[cb][1]), pack_bf16x2(y[cb][2], y[cb][3])};
-        *reinterpret_cast<u32x2*>(Out + 16 * cb + 4 * lg) = pk;
+        u32x4 vu;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          // lane lr of group lg points at key 32cc+16h+4lg+lr/4, channels 16cb+4(lr%4)..+3
+          const int r = 32 * cc + 16 * h + 4 * lg + (lr >> 2);
+          const int chk = 2 * cb + ((lr & 3) >> 1);
+          const u32x2 t2 = lds_read_tr16(vs + r * DV + 8 * T::vchunk(r, chk) + 4 * (lr & 1));
+          vu[2 * h] = t2[0];
+          vu[2 * h + 1] = t2[1];
+        }
+        const bf16x8 va = as_bf16x8(vu);
+#pragma unroll
+        for (int u = 0; u < SUB; ++u) O[u][cb] = mfma16x16x32_bf16(va, pf[u], O[u][cb]);
       }
     }
+  };
+
+  issue_tile(stage0, 0);
+  wait_vmem();
+  __syncthreads();
+  for (int kt = 0; kt < nkt; kt += 2) {
+    if (kt + 1 < nkt) issue_tile(stage1, kt + 1);
+    compute_tile(stage0, kt);
+    wait_vmem();
+    __syncthreads();
+    if (kt + 1 < nkt) {
+      if (kt + 2 < nkt) issue_tile(stage0, kt + 2);
+      compute_tile(stage1, kt + 1);
+      wait_vmem();
+      __syncthreads();
+    }
+  }
+
+  // map-1 wave: Y = O1/l1 - lambda O2/l2 with O2/l2 read from the exchange,
+  // then the norm, the scale and the store
+  auto finish_rows = [&](const float* xch) {
+    const float lam = *a.lambda;
+#pragma unroll
+    for (int u = 0; u < SUB; ++u) {
+      const float i1 = 1.0f / L[u][0];
+      auto o2_at = [&](int cb) { return *reinterpret_cast<const f32x4*>(xch + ((u * CB + cb) * 64 + lane) * 4); };
+      float r = 1.0f;
+      if (NORM) {
+        float ss = 0.f;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          const f32x4 o2 = o2_at(cb);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float yv = O[u][cb][j] * i1 - lam * o2[j];
+            ss += yv * yv;
+          }
+        }
+        ss = sum_over_lane_groups(ss);
+        r = a.out_scale / sqrtf(ss * (1.0f / DV) + a.eps);
+      }
+      const int row = qw0 + 16 * u + lr;
+      if (row < N) {
+        uint16_t* __restrict__ Out = (uint16_t*)a.out + (hrow + row) * DV;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          const f32x4 o2 = o2_at(cb);
+          float y[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int col = 16 * cb + 4 * lg + j;
+            y[j] = (O[u][cb][j] * i1 - lam * o2[j]) * (NORM ? r * (a.norm_w ? a.norm_w[col] : 1.0f) : 1.0f);
+          }
+          u32x2 pk = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+          *reinterpret_cast<u32x2*>(Out + 16 * cb + 4 * lg) = pk;
+        }
+      }
+    }
+  };
+
+  // Epilogue: the map-2 wave of each row group publishes O2/l2 (fp32, in its
+  // lane layout); the map-1 wave forms Y = O1/l1 - lambda O2/l2, normalises
+  // and stores.  Both stage buffers are free after the loop's last barrier.
+  constexpr int XW = 16 * SUB * DV;                     // floats per row group
+  constexpr int PER_STAGE = (T::STAGE * 2) / (XW * 4);  // row groups per stage buffer
+  const int slot = rg % T::XG;
+  float* xch = (float*)(slot < PER_STAGE ? stage0 : stage1) + (slot % PER_STAGE) * XW;
+  for (int phase = 0; phase < (T::WAVES / 2) / T::XG; ++phase) {
+    const bool mine = rg / T::XG == phase;
+    if (mine && mp == 1 && qw0 < N) {
+#pragma unroll
+      for (int u = 0; u < SUB; ++u) {
+        const float il = 1.0f / L[u][0];
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+          *reinterpret_cast<f32x4*>(xch + ((u * CB + cb) * 64 + lane) * 4) = O[u][cb] * il;
+      }
+    }
+    __syncthreads();
+    if (mine && mp == 0 && qw0 < N) finish_rows(xch);
+    __syncthreads();
   }
 }
 
