@@ -24,6 +24,8 @@
 // 4*(L/16)+j, so a lane owns one query's scores for 4 keys per 16-key block
 // and one query's outputs for 4 channels per 16-channel block.
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -261,10 +263,11 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(PrefillArgs a) {
   const u32x4 ones_u = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
   const bf16x8 ones = as_bf16x8(ones_u);
 
-  auto compute_tile = [&](const uint16_t* stg, int kt) {
-    const int kb = kt * BN;
-    if (qw0 >= N || (CAUSAL && kb > qw0 + 16 * SUB - 1)) return;  // nothing visible for this wave
-    const bool need_mask = (CAUSAL && kb + BN - 1 > qw0) || (kb + BN > N);
+  // One key tile.  MASK: the tile holds keys past some row's diagonal or
+  // past N; those tiles take a separate instantiation so that the common
+  // unmasked tiles carry no per-element compare/select work.
+  auto tile_body = [&](const uint16_t* stg, int kb, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const uint16_t* ks_ = stg + mp * KTILE;
     const uint16_t* vs = stg + 2 * KTILE;
 
@@ -288,7 +291,7 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(PrefillArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           float x = acc[u][j];
-          if (need_mask) {
+          if (MASK) {
             const int kabs = kb + 16 * b + 4 * lg + j;
             const int qabs = qw0 + 16 * u + lr;
             x = ((kabs < N) && (!CAUSAL || kabs <= qabs)) ? x : -INFINITY;
@@ -333,6 +336,14 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(PrefillArgs a) {
         for (int u = 0; u < SUB; ++u) O[u][cb] = mfma16x16x32_bf16(va, pf[u], O[u][cb]);
       }
     }
+  };
+  auto compute_tile = [&](const uint16_t* stg, int kt) {
+    const int kb = kt * BN;
+    if (qw0 >= N || (CAUSAL && kb > qw0 + 16 * SUB - 1)) return;  // nothing visible for this wave
+    if ((CAUSAL && kb + BN - 1 > qw0) || (kb + BN > N))
+      tile_body(stg, kb, std::true_type{});
+    else
+      tile_body(stg, kb, std::false_type{});
   };
 
   issue_tile(stage0, 0);
