@@ -89,10 +89,10 @@ diffattn_status diffattn_fwd(diffattn_dtype dt, const void* q1, const void* k1, 
   if (norm_weight && !aligned(norm_weight, 4)) return DIFFATTN_EINVAL;
   const long long BH = (long long)B * H;
   const bool bf16 = dt == DIFFATTN_BF16;
-  const int bm = diffattn::prefill_block_rows(bf16);
+  const int bm = diffattn::prefill_block_rows(bf16, d);
   const long long qtiles = ((long long)N + bm - 1) / bm;
   // one workgroup per (query tile, head); a launch holds at most 2^32 - 1 work-items
-  if (BH > INT32_MAX || qtiles * BH * diffattn::prefill_block_threads(bf16) > (long long)UINT32_MAX)
+  if (BH > INT32_MAX || qtiles * BH * diffattn::prefill_block_threads(bf16, d) > (long long)UINT32_MAX)
     return DIFFATTN_EINVAL;
 
   diffattn::PrefillArgs a;

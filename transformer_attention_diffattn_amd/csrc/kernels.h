@@ -43,8 +43,8 @@ struct DecodeArgs {
 };
 
 // Query rows and threads per workgroup of the prefill kernels.
-int prefill_block_rows(bool bf16);
-int prefill_block_threads(bool bf16);
+int prefill_block_rows(bool bf16, int d);
+int prefill_block_threads(bool bf16, int d);
 
 hipError_t launch_lambda(const float* lq1, const float* lk1, const float* lq2, const float* lk2,
                          int d, float lambda_init, float* out, hipStream_t stream);

@@ -97,26 +97,35 @@ __device__ __forceinline__ void epilogue_values(const f32x4 (&O1)[CB], const f32
 // hands O2/l2 to the map-1 wave through LDS.  K1, K2 and V tiles of BN keys
 // arrive by direct global->LDS loads into two stage buffers (the next tile
 // loads while the current one is consumed).  Rows are XOR-swizzled in 16-byte
-// chunks so that fragment reads are free of bank conflicts; V stays row-major
-// and its transposed fragments come from the transposing LDS read
-// (ds_read_b64_tr_b16).
+// chunks so that K fragment reads are free of bank conflicts.  A V tile is
+// stored as [16-channel block][key][16 channels]: the transposing LDS read
+// (ds_read_b64_tr_b16) of a V^T fragment then covers 512 contiguous bytes,
+// and every such read of a wave uses one address register plus an immediate.
+
+// Shape per head width: waves per workgroup (two per row group), 16-row
+// sub-tiles per wave, keys per tile.
+template <int D>
+struct Bf16Cfg {
+  static constexpr int WAVES = 8;
+  static constexpr int SUB = 2;
+  static constexpr int BN = D >= 128 ? 32 : 64;  // d = 128: keeps a wave within 256 registers
+};
 
 template <int D>
 struct Bf16Tile {
   static constexpr int DV = 2 * D;
-  static constexpr int WAVES = 8;           // 4 row groups x 2 maps
-  static constexpr int SUB = 2;             // 16-row sub-tiles per wave
+  static constexpr int WAVES = Bf16Cfg<D>::WAVES;  // row groups x 2 maps
+  static constexpr int SUB = Bf16Cfg<D>::SUB;      // 16-row sub-tiles per wave
   static constexpr int BM = 16 * SUB * (WAVES / 2);
-  static constexpr int BN = D >= 128 ? 32 : 64;  // d = 128: keeps a wave within 256 registers
+  static constexpr int BN = Bf16Cfg<D>::BN;
   static constexpr int KS = (D + 31) / 32;  // 32-wide k-steps of the QK^T MFMA
   static constexpr int NB = BN / 16;        // 16-key score blocks per tile
   static constexpr int NC = BN / 32;        // 32-key PV k-steps per tile
   static constexpr int CB = DV / 16;        // 16-channel output blocks
   static constexpr int NCH = D / 8;         // 16-byte chunks per K row
-  static constexpr int NCV = DV / 8;        // 16-byte chunks per V row
   static constexpr int RPK = NCH >= 16 ? 1 : 16 / NCH;  // K rows per 256 bytes
   static constexpr int KSEG = BN * NCH / 64;            // 1 KB segments per K tile
-  static constexpr int VSEG = BN * NCV / 64;
+  static constexpr int VSEG = CB * BN / 32;             // 1 KB = 32 keys of one channel block
   static constexpr int NSEG = 2 * KSEG + VSEG;
   static constexpr int KTILE = BN * D;  // elements
   static constexpr int VTILE = BN * DV;
@@ -130,11 +139,6 @@ struct Bf16Tile {
 
   // physical 16-byte chunk of logical chunk c in K row r
   static __device__ __forceinline__ int kchunk(int r, int c) { return c ^ ((r / RPK) % NCH); }
-  // physical 16-byte chunk of logical chunk c in V row r: the four rows of a
-  // transposed read land on distinct banks
-  static __device__ __forceinline__ int vchunk(int r, int c) {
-    return (DV * 2 >= 128) ? (c ^ (2 * (r & 3))) : (c ^ (2 * ((r >> 1) & 1)));
-  }
 };
 
 typedef __attribute__((ext_vector_type(4))) short s16x4;
@@ -146,6 +150,25 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
 }
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Byte offset of an LDS location (wave-uniform callers only).
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)DIFFATTN_LDS(p));
+}
+
+// 16 bytes per lane from global memory straight into LDS at lds + 16*lane
+// (global_load_lds_dwordx4).  Issued through asm so that the compiler does
+// not track it: it would otherwise wait for every outstanding tile before
+// any LDS read.  Completion is awaited explicitly with s_waitcnt vmcnt plus
+// a workgroup barrier before the data is read.
+__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds) : "memory", "m0");
+}
+// wait until at most K vector-memory operations of this wave are outstanding
+template <int K>
+__device__ __forceinline__ void wait_vmem_keep() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(K) : "memory");
+}
 
 // max over lanes l, l^16, l^32, l^48 without LDS traffic (v_permlane*_swap)
 __device__ __forceinline__ float max4_groups(float x) {
@@ -179,13 +202,14 @@ __device__ __forceinline__ void softmax_raw(float (&s)[NT], float c, float& m, f
 }
 
 template <int D, bool CAUSAL, bool NORM>
-__global__ __launch_bounds__(512) void prefill_bf16_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(PrefillArgs a) {
   using T = Bf16Tile<D>;
   constexpr int DV = T::DV, BN = T::BN, KS = T::KS, NB = T::NB, NC = T::NC, CB = T::CB, SUB = T::SUB;
-  constexpr int NCH = T::NCH, NCV = T::NCV, KSEG = T::KSEG, KTILE = T::KTILE;
+  constexpr int NCH = T::NCH, KSEG = T::KSEG, KTILE = T::KTILE;
 
   __shared__ __attribute__((aligned(16))) uint16_t stage0[T::STAGE];
   __shared__ __attribute__((aligned(16))) uint16_t stage1[T::STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t stage2[T::STAGE];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -219,6 +243,12 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(PrefillArgs a) {
       qf[u][ks] = as_bf16x8(dc < D ? ld16(Qm + (size_t)qrow * D + dc) : zero_u32x4());
     }
   }
+  // Settle the Q loads here: otherwise their first use inside the key loop
+  // carries a vmcnt(0) wait that would also drain the tile prefetches.
+#pragma unroll
+  for (int u = 0; u < SUB; ++u)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qf[u][ks]));
 
   const int kend = CAUSAL ? min(N, q0 + T::BM) : N;
   const int nkt = (kend + BN - 1) / BN;
@@ -240,13 +270,15 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(PrefillArgs a) {
         src = (mtx ? K2 : K1) + (size_t)min(kb + r, N - 1) * D + 8 * c;
         ldst = dst + mtx * KTILE + sg * 512;
       } else {
+        // segment sg: keys 32*(sg % (BN/32)).. of channel block sg / (BN/32);
+        // lane: key +lane/2, channels +8*(lane&1)
         const int sg = seg - 2 * KSEG;
-        const int r = sg * (64 / NCV) + lane / NCV;
-        const int c = T::vchunk(r, lane % NCV);
-        src = V + (size_t)min(kb + r, N - 1) * DV + 8 * c;
+        const int cb = sg / (BN / 32);
+        const int r = 32 * (sg % (BN / 32)) + (lane >> 1);
+        src = V + (size_t)min(kb + r, N - 1) * DV + 16 * cb + 8 * (lane & 1);
         ldst = dst + 2 * KTILE + sg * 512;
       }
-      __builtin_amdgcn_global_load_lds(src, DIFFATTN_LDS(ldst), 16, 0, 0);
+      lds_dma16(src, lds_offset(ldst));
     }
   };
 
@@ -300,8 +332,36 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(PrefillArgs a) {
         }
     }
 
+    // running maxima: one rescale branch per tile for both sub-tiles
+    {
+      float mt[SUB];
+      bool need = false;
 #pragma unroll
-    for (int u = 0; u < SUB; ++u) softmax_raw<4 * NB, CB>(s[u], c, m[u], L[u], O[u]);
+      for (int u = 0; u < SUB; ++u) {
+        float x = s[u][0];
+#pragma unroll
+        for (int i = 1; i < 4 * NB; ++i) x = fmaxf(x, s[u][i]);
+        mt[u] = max4_groups(x) * c;
+        need |= mt[u] > m[u] + kRescaleThreshold;
+      }
+      if (wave_any(need)) {
+#pragma unroll
+        for (int u = 0; u < SUB; ++u) {
+          const float mn = fmaxf(m[u], mt[u]);
+          const float alpha = (mn == -INFINITY) ? 1.0f : exp2_fast(m[u] - mn);
+          m[u] = mn;
+          L[u] *= alpha;
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) O[u][cb] *= alpha;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < SUB; ++u) {
+        const float nm = -m[u];
+#pragma unroll
+        for (int i = 0; i < 4 * NB; ++i) s[u][i] = exp2_fast(__builtin_fmaf(s[u][i], c, nm));
+      }
+    }
 
     // O^T += V^T P^T: P^T fragment of chunk cc = blocks 2cc (e 0..3) and 2cc+1 (e 4..7)
 #pragma unroll
@@ -324,10 +384,10 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(PrefillArgs a) {
         u32x4 vu;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          // lane lr of group lg points at key 32cc+16h+4lg+lr/4, channels 16cb+4(lr%4)..+3
-          const int r = 32 * cc + 16 * h + 4 * lg + (lr >> 2);
-          const int chk = 2 * cb + ((lr & 3) >> 1);
-          const u32x2 t2 = lds_read_tr16(vs + r * DV + 8 * T::vchunk(r, chk) + 4 * (lr & 1));
+          // lane lr of group lg points at key 32cc+16h+4lg+lr/4, channels
+          // 16cb+4(lr%4)..+3: in the [block][key][16] layout that is
+          // element 16*(BN*cb + 32cc + 16h) + 4*lane
+          const u32x2 t2 = lds_read_tr16(vs + 16 * (BN * cb + 32 * cc + 16 * h) + 4 * lane);
           vu[2 * h] = t2[0];
           vu[2 * h + 1] = t2[1];
         }
@@ -346,21 +406,27 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(PrefillArgs a) {
       tile_body(stg, kb, std::false_type{});
   };
 
-  issue_tile(stage0, 0);
-  wait_vmem();
-  __syncthreads();
-  for (int kt = 0; kt < nkt; kt += 2) {
-    if (kt + 1 < nkt) issue_tile(stage1, kt + 1);
-    compute_tile(stage0, kt);
-    wait_vmem();
-    __syncthreads();
-    if (kt + 1 < nkt) {
-      if (kt + 2 < nkt) issue_tile(stage0, kt + 2);
-      compute_tile(stage1, kt + 1);
+  // Three-stage ring: entering step kt, tiles kt and kt+1 are in flight.
+  // Wait for tile kt only (the newer loads may stay outstanding), then a
+  // barrier: everybody's tile kt has landed and nobody still reads stage
+  // `aft`, which receives tile kt+2.
+  auto step = [&](const uint16_t* cur, uint16_t* aft, int kt) {
+    if (kt + 1 < nkt)
+      wait_vmem_keep<T::NSEG / T::WAVES>();
+    else
       wait_vmem();
-      __syncthreads();
-    }
+    __syncthreads();
+    if (kt + 2 < nkt) issue_tile(aft, kt + 2);
+    compute_tile(cur, kt);
+  };
+  issue_tile(stage0, 0);
+  if (nkt > 1) issue_tile(stage1, 1);
+  for (int kt = 0; kt < nkt; kt += 3) {
+    step(stage0, stage2, kt);
+    if (kt + 1 < nkt) step(stage1, stage0, kt + 1);
+    if (kt + 2 < nkt) step(stage2, stage1, kt + 2);
   }
+  __syncthreads();  // all reads of the stage buffers are done
 
   // map-1 wave: Y = O1/l1 - lambda O2/l2 with O2/l2 read from the exchange,
   // then the norm, the scale and the store
@@ -609,13 +675,29 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillArgs a) {
 // ---------------------------------------------------------------------------
 // dispatch
 
-int prefill_block_rows(bool bf16) { return bf16 ? 128 : 64; }
-int prefill_block_threads(bool bf16) { return bf16 ? 512 : 256; }
+int prefill_block_rows(bool bf16, int d) {
+  if (!bf16) return 64;
+  switch (d) {
+    case 16: return Bf16Tile<16>::BM;
+    case 32: return Bf16Tile<32>::BM;
+    case 64: return Bf16Tile<64>::BM;
+    default: return Bf16Tile<128>::BM;
+  }
+}
+int prefill_block_threads(bool bf16, int d) {
+  if (!bf16) return 256;
+  switch (d) {
+    case 16: return 64 * Bf16Tile<16>::WAVES;
+    case 32: return 64 * Bf16Tile<32>::WAVES;
+    case 64: return 64 * Bf16Tile<64>::WAVES;
+    default: return 64 * Bf16Tile<128>::WAVES;
+  }
+}
 
 template <int D, bool C, bool NM>
 static hipError_t launch_one(bool bf16, const PrefillArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)a.n_qtiles * (unsigned)a.BH);
-  const dim3 block(prefill_block_threads(bf16));
+  const dim3 block(prefill_block_threads(bf16, D));
   if (bf16)
     hipLaunchKernelGGL((prefill_bf16_kernel<D, C, NM>), grid, block, 0, s, a);
   else
