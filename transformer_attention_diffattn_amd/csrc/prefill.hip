@@ -109,6 +109,8 @@ struct Bf16Cfg {
   static constexpr int WAVES = 8;
   static constexpr int SUB = 2;
   static constexpr int BN = D >= 128 ? 32 : 64;  // d = 128: keeps a wave within 256 registers
+  static constexpr int STAGES = 2;  // LDS stage buffers (2 or 3)
+  static constexpr int PV_FENCE = D >= 128 ? 4 : 0;  // channel blocks between scheduling fences
 };
 
 template <int D>
@@ -118,6 +120,8 @@ struct Bf16Tile {
   static constexpr int SUB = Bf16Cfg<D>::SUB;      // 16-row sub-tiles per wave
   static constexpr int BM = 16 * SUB * (WAVES / 2);
   static constexpr int BN = Bf16Cfg<D>::BN;
+  static constexpr int STAGES = Bf16Cfg<D>::STAGES;
+  static constexpr int PV_FENCE = Bf16Cfg<D>::PV_FENCE;
   static constexpr int KS = (D + 31) / 32;  // 32-wide k-steps of the QK^T MFMA
   static constexpr int NB = BN / 16;        // 16-key score blocks per tile
   static constexpr int NC = BN / 32;        // 32-key PV k-steps per tile
@@ -131,11 +135,6 @@ struct Bf16Tile {
   static constexpr int VTILE = BN * DV;
   static constexpr int STAGE = 2 * KTILE + VTILE;
   static_assert(NSEG % WAVES == 0, "segments split evenly over the waves");
-  // The epilogue exchange (fp32 O2/l2, 16*SUB*DV floats per row group)
-  // reuses both stage buffers, XG row groups at a time.
-  static constexpr int XG_FIT = (2 * STAGE * 2) / (16 * SUB * DV * 4);
-  static constexpr int XG = XG_FIT >= WAVES / 2 ? WAVES / 2 : XG_FIT;
-  static_assert(XG >= 1 && (WAVES / 2) % XG == 0, "exchange phases");
 
   // physical 16-byte chunk of logical chunk c in K row r
   static __device__ __forceinline__ int kchunk(int r, int c) { return c ^ ((r / RPK) % NCH); }
@@ -206,58 +205,79 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
   using T = Bf16Tile<D>;
   constexpr int DV = T::DV, BN = T::BN, KS = T::KS, NB = T::NB, NC = T::NC, CB = T::CB, SUB = T::SUB;
   constexpr int NCH = T::NCH, KSEG = T::KSEG, KTILE = T::KTILE;
+  constexpr int RG = T::WAVES / 2;  // row groups
 
-  __shared__ __attribute__((aligned(16))) uint16_t stage0[T::STAGE];
-  __shared__ __attribute__((aligned(16))) uint16_t stage1[T::STAGE];
-  __shared__ __attribute__((aligned(16))) uint16_t stage2[T::STAGE];
+  constexpr int STAGES = T::STAGES;
+  __shared__ __attribute__((aligned(16))) uint16_t stages[STAGES * T::STAGE];
+  __shared__ float wsh[DV];  // norm weight
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // wave-uniform values live in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int mp = wave & 1;   // which map this wave computes
   const int rg = wave >> 1;  // row group
   const int lr = lane & 15;  // query column of the 16x16 blocks owned by this lane
   const int lg = lane >> 4;  // lane group: rows 4*lg..4*lg+3 of each block
   const int N = a.N;
+  const float c = a.c;
+  const float lam = *a.lambda;
+  for (int i = threadIdx.x; i < DV; i += blockDim.x) wsh[i] = a.norm_w ? a.norm_w[i] : 1.0f;
 
-  // longest query tiles first under the causal mask; heads vary fastest
-  const int bid = blockIdx.x;
-  const int bh = bid % a.BH;
-  const int qt = CAUSAL ? (a.n_qtiles - 1 - bid / a.BH) : (bid / a.BH);
-  const int q0 = qt * T::BM;
-  const int qw0 = q0 + 16 * SUB * rg;
+  // Persistent schedule: work items (query tile, head) are ordered longest
+  // first under the causal mask, heads fastest; workgroup g takes one item
+  // per round of G items, walking the rounds in alternating directions so
+  // that every workgroup's total is about the same.  When G is a multiple of
+  // B*H only the tile order is reversed, keeping each head on one workgroup
+  // position (and so on one XCD's L2).
+  const int G = gridDim.x, g = blockIdx.x, BH = a.BH;
+  const long long n_items = (long long)a.n_qtiles * BH;
+  auto item_at = [&](int r) -> long long {
+    int pos = g;
+    if (r & 1) pos = (G % BH == 0) ? ((G / BH - 1 - g / BH) * BH + g % BH) : (G - 1 - g);
+    const long long i = (long long)r * G + pos;
+    return i < n_items ? i : -1;
+  };
 
-  const size_t hrow = (size_t)bh * (size_t)N;
-  const uint16_t* __restrict__ Qm = (const uint16_t*)(mp ? a.q2 : a.q1) + hrow * D;
-  const uint16_t* __restrict__ K1 = (const uint16_t*)a.k1 + hrow * D;
-  const uint16_t* __restrict__ K2 = (const uint16_t*)a.k2 + hrow * D;
-  const uint16_t* __restrict__ V = (const uint16_t*)a.v + hrow * DV;
+  // the current and the next item
+  struct Item {
+    int bh, q0, qw0, nkt;
+    size_t hrow;
+  };
+  auto decode_item = [&](long long i) {
+    Item it;
+    it.bh = (int)(i % BH);
+    const int qt = (int)(CAUSAL ? (a.n_qtiles - 1 - i / BH) : (i / BH));
+    it.q0 = qt * T::BM;
+    it.qw0 = it.q0 + 16 * SUB * rg;
+    const int kend = CAUSAL ? min(N, it.q0 + T::BM) : N;
+    it.nkt = (kend + BN - 1) / BN;
+    it.hrow = (size_t)it.bh * (size_t)N;
+    return it;
+  };
 
   // Q^T fragments (B operand of S^T = K Q^T): dims 32ks+8lg..+7 of the row
   bf16x8 qf[SUB][KS];
+  auto load_q = [&](const Item& it) {
+    const uint16_t* Qm = (const uint16_t*)(mp ? a.q2 : a.q1) + it.hrow * D;
 #pragma unroll
-  for (int u = 0; u < SUB; ++u) {
-    const int qrow = min(qw0 + 16 * u + lr, N - 1);
+    for (int u = 0; u < SUB; ++u) {
+      const int qrow = min(it.qw0 + 16 * u + lr, N - 1);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int dc = 32 * ks + 8 * lg;
-      qf[u][ks] = as_bf16x8(dc < D ? ld16(Qm + (size_t)qrow * D + dc) : zero_u32x4());
+      for (int ks = 0; ks < KS; ++ks) {
+        const int dc = 32 * ks + 8 * lg;
+        qf[u][ks] = as_bf16x8(dc < D ? ld16(Qm + (size_t)qrow * D + dc) : zero_u32x4());
+      }
     }
-  }
-  // Settle the Q loads here: otherwise their first use inside the key loop
-  // carries a vmcnt(0) wait that would also drain the tile prefetches.
-#pragma unroll
-  for (int u = 0; u < SUB; ++u)
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qf[u][ks]));
-
-  const int kend = CAUSAL ? min(N, q0 + T::BM) : N;
-  const int nkt = (kend + BN - 1) / BN;
+  };
 
   // Direct global->LDS loads of one key tile: each instruction moves 1 KB
   // (64 lanes x 16 B) to consecutive LDS; a lane fetches the global chunk
   // that the swizzle assigns to its LDS position.
-  auto issue_tile = [&](uint16_t* dst, int kt) {
+  auto issue_tile = [&](uint16_t* dst, const Item& it, int kt) {
     const int kb = kt * BN;
+    const uint16_t* K1 = (const uint16_t*)a.k1 + it.hrow * D;
+    const uint16_t* K2 = (const uint16_t*)a.k2 + it.hrow * D;
+    const uint16_t* V = (const uint16_t*)a.v + it.hrow * DV;
 #pragma unroll
     for (int i = 0; i < T::NSEG / T::WAVES; ++i) {
       const int seg = wave + i * T::WAVES;
@@ -266,8 +286,8 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
       if (seg < 2 * KSEG) {
         const int mtx = seg / KSEG, sg = seg % KSEG;
         const int r = sg * (64 / NCH) + lane / NCH;
-        const int c = T::kchunk(r, lane % NCH);
-        src = (mtx ? K2 : K1) + (size_t)min(kb + r, N - 1) * D + 8 * c;
+        const int cch = T::kchunk(r, lane % NCH);
+        src = (mtx ? K2 : K1) + (size_t)min(kb + r, N - 1) * D + 8 * cch;
         ldst = dst + mtx * KTILE + sg * 512;
       } else {
         // segment sg: keys 32*(sg % (BN/32)).. of channel block sg / (BN/32);
@@ -284,21 +304,13 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
 
   f32x4 O[SUB][CB], L[SUB];
   float m[SUB];
-#pragma unroll
-  for (int u = 0; u < SUB; ++u) {
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) O[u][cb] = zero_f32x4();
-    L[u] = zero_f32x4();
-    m[u] = -INFINITY;
-  }
-  const float c = a.c;
   const u32x4 ones_u = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
   const bf16x8 ones = as_bf16x8(ones_u);
 
   // One key tile.  MASK: the tile holds keys past some row's diagonal or
   // past N; those tiles take a separate instantiation so that the common
   // unmasked tiles carry no per-element compare/select work.
-  auto tile_body = [&](const uint16_t* stg, int kb, auto mask_tag) {
+  auto tile_body = [&](const uint16_t* stg, int kb, int qw0, auto mask_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const uint16_t* ks_ = stg + mp * KTILE;
     const uint16_t* vs = stg + 2 * KTILE;
@@ -394,75 +406,50 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
         const bf16x8 va = as_bf16x8(vu);
 #pragma unroll
         for (int u = 0; u < SUB; ++u) O[u][cb] = mfma16x16x32_bf16(va, pf[u], O[u][cb]);
+        // keep the scheduler from hoisting every V fragment read at once
+        if (T::PV_FENCE > 0 && cb % T::PV_FENCE == T::PV_FENCE - 1) __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
-  auto compute_tile = [&](const uint16_t* stg, int kt) {
+  auto compute_tile = [&](const uint16_t* stg, const Item& it, int kt) {
     const int kb = kt * BN;
-    if (qw0 >= N || (CAUSAL && kb > qw0 + 16 * SUB - 1)) return;  // nothing visible for this wave
-    if ((CAUSAL && kb + BN - 1 > qw0) || (kb + BN > N))
-      tile_body(stg, kb, std::true_type{});
+    if (it.qw0 >= N || (CAUSAL && kb > it.qw0 + 16 * SUB - 1)) return;  // nothing visible for this wave
+    if ((CAUSAL && kb + BN - 1 > it.qw0) || (kb + BN > N))
+      tile_body(stg, kb, it.qw0, std::true_type{});
     else
-      tile_body(stg, kb, std::false_type{});
+      tile_body(stg, kb, it.qw0, std::false_type{});
   };
-
-  // Three-stage ring: entering step kt, tiles kt and kt+1 are in flight.
-  // Wait for tile kt only (the newer loads may stay outstanding), then a
-  // barrier: everybody's tile kt has landed and nobody still reads stage
-  // `aft`, which receives tile kt+2.
-  auto step = [&](const uint16_t* cur, uint16_t* aft, int kt) {
-    if (kt + 1 < nkt)
-      wait_vmem_keep<T::NSEG / T::WAVES>();
-    else
-      wait_vmem();
-    __syncthreads();
-    if (kt + 2 < nkt) issue_tile(aft, kt + 2);
-    compute_tile(cur, kt);
-  };
-  issue_tile(stage0, 0);
-  if (nkt > 1) issue_tile(stage1, 1);
-  for (int kt = 0; kt < nkt; kt += 3) {
-    step(stage0, stage2, kt);
-    if (kt + 1 < nkt) step(stage1, stage0, kt + 1);
-    if (kt + 2 < nkt) step(stage2, stage1, kt + 2);
-  }
-  __syncthreads();  // all reads of the stage buffers are done
 
   // map-1 wave: Y = O1/l1 - lambda O2/l2 with O2/l2 read from the exchange,
   // then the norm, the scale and the store
-  auto finish_rows = [&](const float* xch) {
-    const float lam = *a.lambda;
+  auto finish_rows = [&](const Item& it, const float* xch) {
 #pragma unroll
     for (int u = 0; u < SUB; ++u) {
+      // O becomes Y in place: one pass over the exchange, no second copy
       const float i1 = 1.0f / L[u][0];
-      auto o2_at = [&](int cb) { return *reinterpret_cast<const f32x4*>(xch + ((u * CB + cb) * 64 + lane) * 4); };
+      float ss = 0.f;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const f32x4 o2 = *reinterpret_cast<const f32x4*>(xch + ((u * CB + cb) * 64 + lane) * 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          O[u][cb][j] = O[u][cb][j] * i1 - lam * o2[j];
+          ss += O[u][cb][j] * O[u][cb][j];
+        }
+      }
       float r = 1.0f;
       if (NORM) {
-        float ss = 0.f;
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-          const f32x4 o2 = o2_at(cb);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float yv = O[u][cb][j] * i1 - lam * o2[j];
-            ss += yv * yv;
-          }
-        }
         ss = sum_over_lane_groups(ss);
         r = a.out_scale / sqrtf(ss * (1.0f / DV) + a.eps);
       }
-      const int row = qw0 + 16 * u + lr;
+      const int row = it.qw0 + 16 * u + lr;
       if (row < N) {
-        uint16_t* __restrict__ Out = (uint16_t*)a.out + (hrow + row) * DV;
+        uint16_t* __restrict__ Out = (uint16_t*)a.out + (it.hrow + row) * DV;
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
-          const f32x4 o2 = o2_at(cb);
           float y[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int col = 16 * cb + 4 * lg + j;
-            y[j] = (O[u][cb][j] * i1 - lam * o2[j]) * (NORM ? r * (a.norm_w ? a.norm_w[col] : 1.0f) : 1.0f);
-          }
+          for (int j = 0; j < 4; ++j) y[j] = O[u][cb][j] * (NORM ? r * wsh[16 * cb + 4 * lg + j] : 1.0f);
           u32x2 pk = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
           *reinterpret_cast<u32x2*>(Out + 16 * cb + 4 * lg) = pk;
         }
@@ -470,27 +457,111 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
     }
   };
 
-  // Epilogue: the map-2 wave of each row group publishes O2/l2 (fp32, in its
-  // lane layout); the map-1 wave forms Y = O1/l1 - lambda O2/l2, normalises
-  // and stores.  Both stage buffers are free after the loop's last barrier.
-  constexpr int XW = 16 * SUB * DV;                     // floats per row group
-  constexpr int PER_STAGE = (T::STAGE * 2) / (XW * 4);  // row groups per stage buffer
-  const int slot = rg % T::XG;
-  float* xch = (float*)(slot < PER_STAGE ? stage0 : stage1) + (slot % PER_STAGE) * XW;
-  for (int phase = 0; phase < (T::WAVES / 2) / T::XG; ++phase) {
-    const bool mine = rg / T::XG == phase;
-    if (mine && mp == 1 && qw0 < N) {
+  // Epilogue of one item in stage buffer `xb` (the one its last tile used;
+  // no load targets it before the epilogue ends): the map-2 wave of each row
+  // group publishes O2/l2 (fp32, in its lane layout), the map-1 wave forms
+  // Y = O1/l1 - lambda O2/l2, normalises and stores; XR row groups per phase.
+  constexpr int XW = 16 * SUB * DV;                  // floats per row group
+  constexpr int XR_FIT = (T::STAGE * 2) / (XW * 4);  // row groups per stage buffer
+  constexpr int XR = XR_FIT >= RG ? RG : XR_FIT;
+  static_assert(XR >= 1 && RG % XR == 0, "exchange phases");
+  auto epilogue = [&](const Item& it, uint16_t* xb) {
+    float* xch = (float*)xb + (rg % XR) * XW;
 #pragma unroll
-      for (int u = 0; u < SUB; ++u) {
-        const float il = 1.0f / L[u][0];
+    for (int ph = 0; ph < RG / XR; ++ph) {
+      const bool mine = rg / XR == ph;
+      if (mine && mp == 1 && it.qw0 < N) {
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
-          *reinterpret_cast<f32x4*>(xch + ((u * CB + cb) * 64 + lane) * 4) = O[u][cb] * il;
+        for (int u = 0; u < SUB; ++u) {
+          const float il = 1.0f / L[u][0];
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb)
+            *reinterpret_cast<f32x4*>(xch + ((u * CB + cb) * 64 + lane) * 4) = O[u][cb] * il;
+        }
       }
+      __syncthreads();
+      if (mine && mp == 0 && it.qw0 < N) finish_rows(it, xch);
+      __syncthreads();
     }
-    __syncthreads();
-    if (mine && mp == 0 && qw0 < N) finish_rows(xch);
-    __syncthreads();
+  };
+
+  // The key tiles of all this workgroup's items form one stream through the
+  // ring of stage buffers; the load cursor runs STAGES-1 tiles ahead of the
+  // compute, across item boundaries.
+  struct Cursor {
+    int r, kt;
+    bool ok;
+    Item it;
+  };
+  int ib = 0;        // stage buffer of the next tile to load
+  int inflight = 0;  // tiles loaded or loading and not yet consumed
+  auto load_next = [&](Cursor& q) {
+    if (!q.ok) return;
+    issue_tile(stages + ib * T::STAGE, q.it, q.kt);
+    ib = ib + 1 == STAGES ? 0 : ib + 1;
+    ++inflight;
+    if (++q.kt < q.it.nkt) return;
+    q.kt = 0;
+    const long long i = item_at(++q.r);
+    q.ok = i >= 0;
+    if (q.ok) q.it = decode_item(i);
+  };
+
+  // The Q rows of an item come in through ordinary loads that the compiler
+  // waits for itself; the empty asm makes that wait happen here, once per
+  // item, where waiting for everything outstanding costs nothing, instead
+  // of inside the tile loop.
+  auto settle_q = [&]() {
+#pragma unroll
+    for (int u = 0; u < SUB; ++u)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qf[u][ks]));
+  };
+
+  int r = 0;
+  const long long i0 = item_at(0);
+  if (i0 < 0) return;
+  Item cur = decode_item(i0);
+  Cursor ld{0, 0, true, cur};
+  load_next(ld);
+  load_q(cur);
+  settle_q();
+#pragma unroll
+  for (int p = 1; p < STAGES - 1; ++p) load_next(ld);
+  int cbf = 0;  // stage buffer of the tile being consumed
+  while (true) {
+#pragma unroll
+    for (int u = 0; u < SUB; ++u) {
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) O[u][cb] = zero_f32x4();
+      L[u] = zero_f32x4();
+      m[u] = -INFINITY;
+    }
+    for (int kt = 0; kt < cur.nkt; ++kt) {
+      // this wave's loads of tile kt have landed (a newer tile may still be
+      // loading: it is the newest vector-memory work of the wave)
+      if (STAGES > 2 && __builtin_amdgcn_readfirstlane(inflight) > 1)
+        wait_vmem_keep<T::NSEG / T::WAVES>();
+      else
+        wait_vmem();
+      __syncthreads();  // ... everybody's, and nobody still reads the buffer the next load reuses
+      // With three or more stages the load that follows an item's last tile
+      // waits until after the epilogue, so that it stays the newest.
+      if (STAGES == 2 || kt + 1 < cur.nkt) load_next(ld);
+      compute_tile(stages + cbf * T::STAGE, cur, kt);
+      --inflight;
+      cbf = cbf + 1 == STAGES ? 0 : cbf + 1;
+    }
+    const long long ni = item_at(r + 1);
+    const Item nxt = decode_item(ni < 0 ? i0 : ni);
+    if (ni >= 0) load_q(nxt);  // the last tile's QK^T is done: qf is free
+    __syncthreads();           // everybody is done with the last tile's buffer
+    epilogue(cur, stages + (cbf == 0 ? STAGES - 1 : cbf - 1) * T::STAGE);
+    settle_q();
+    if (STAGES > 2) load_next(ld);
+    if (ni < 0) break;
+    cur = nxt;
+    ++r;
   }
 }
 
@@ -696,12 +767,19 @@ int prefill_block_threads(bool bf16, int d) {
 
 template <int D, bool C, bool NM>
 static hipError_t launch_one(bool bf16, const PrefillArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)a.n_qtiles * (unsigned)a.BH);
+  const long long items = (long long)a.n_qtiles * (long long)a.BH;
   const dim3 block(prefill_block_threads(bf16, D));
-  if (bf16)
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, C, NM>), grid, block, 0, s, a);
-  else
-    hipLaunchKernelGGL((prefill_f32_kernel<D, C, NM>), grid, block, 0, s, a);
+  if (bf16) {
+    // persistent: one workgroup per compute unit walks the item list
+    int dev = 0, ncu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const long long grid = items < ncu ? items : (ncu > 0 ? ncu : 1);
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, C, NM>), dim3((unsigned)grid), block, 0, s, a);
+  } else {
+    hipLaunchKernelGGL((prefill_f32_kernel<D, C, NM>), dim3((unsigned)items), block, 0, s, a);
+  }
   return hipGetLastError();
 }
 
