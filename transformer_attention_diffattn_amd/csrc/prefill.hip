@@ -109,7 +109,11 @@ struct Bf16Cfg {
   static constexpr int WAVES = 8;
   static constexpr int SUB = 2;
   static constexpr int BN = D >= 128 ? 32 : 64;  // d = 128: keeps a wave within 256 registers
-  static constexpr int STAGES = 2;  // LDS stage buffers (2 or 3)
+  // Software-pipelined tile loop (QK^T of the next tile overlaps the
+  // softmax of the current one); d = 128 has no registers to spare for the
+  // second tile's scores and runs the phases of a tile in sequence.
+  static constexpr bool PIPE = D <= 64;
+  static constexpr int STAGES = PIPE ? 3 : 2;  // LDS stage buffers
   static constexpr int PV_FENCE = D >= 128 ? 4 : 0;  // channel blocks between scheduling fences
 };
 
@@ -121,6 +125,8 @@ struct Bf16Tile {
   static constexpr int BM = 16 * SUB * (WAVES / 2);
   static constexpr int BN = Bf16Cfg<D>::BN;
   static constexpr int STAGES = Bf16Cfg<D>::STAGES;
+  static constexpr bool PIPE = Bf16Cfg<D>::PIPE;
+  static_assert(STAGES == (PIPE ? 3 : 2), "stage ring of the tile loop");
   static constexpr int PV_FENCE = Bf16Cfg<D>::PV_FENCE;
   static constexpr int KS = (D + 31) / 32;  // 32-wide k-steps of the QK^T MFMA
   static constexpr int NB = BN / 16;        // 16-key score blocks per tile
@@ -162,6 +168,15 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
 // a workgroup barrier before the data is read.
 __device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds) : "memory", "m0");
+}
+// The same with a wave-uniform 64-bit base (scalar registers) and a 32-bit
+// per-lane byte offset.
+__device__ __forceinline__ void lds_dma16_s(const void* base, uint32_t off, uint32_t lds) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  const uint64_t ub = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t ul = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(ub), "s"(ul) : "memory", "m0");
 }
 // wait until at most K vector-memory operations of this wave are outstanding
 template <int K>
@@ -230,35 +245,35 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
   // B*H only the tile order is reversed, keeping each head on one workgroup
   // position (and so on one XCD's L2).
   const int G = gridDim.x, g = blockIdx.x, BH = a.BH;
-  const long long n_items = (long long)a.n_qtiles * BH;
-  auto item_at = [&](int r) -> long long {
+  const int n_items = a.n_qtiles * BH;  // below 2^31 (checked by the host)
+  auto item_at = [&](int r) -> int {
     int pos = g;
     if (r & 1) pos = (G % BH == 0) ? ((G / BH - 1 - g / BH) * BH + g % BH) : (G - 1 - g);
-    const long long i = (long long)r * G + pos;
+    const int i = r * G + pos;
     return i < n_items ? i : -1;
   };
 
-  // the current and the next item
+  // One item; every field is wave-uniform and kept in scalar registers.
   struct Item {
     int bh, q0, qw0, nkt;
-    size_t hrow;
   };
-  auto decode_item = [&](long long i) {
+  auto decode_item = [&](int i) {
     Item it;
-    it.bh = (int)(i % BH);
-    const int qt = (int)(CAUSAL ? (a.n_qtiles - 1 - i / BH) : (i / BH));
+    const int qi = __builtin_amdgcn_readfirstlane(i / BH);
+    it.bh = __builtin_amdgcn_readfirstlane(i - qi * BH);
+    const int qt = CAUSAL ? a.n_qtiles - 1 - qi : qi;
     it.q0 = qt * T::BM;
     it.qw0 = it.q0 + 16 * SUB * rg;
     const int kend = CAUSAL ? min(N, it.q0 + T::BM) : N;
     it.nkt = (kend + BN - 1) / BN;
-    it.hrow = (size_t)it.bh * (size_t)N;
     return it;
   };
+  auto head_row = [&](const Item& it) { return (size_t)it.bh * (size_t)N; };
 
   // Q^T fragments (B operand of S^T = K Q^T): dims 32ks+8lg..+7 of the row
   bf16x8 qf[SUB][KS];
   auto load_q = [&](const Item& it) {
-    const uint16_t* Qm = (const uint16_t*)(mp ? a.q2 : a.q1) + it.hrow * D;
+    const uint16_t* Qm = (const uint16_t*)(mp ? a.q2 : a.q1) + head_row(it) * D;
 #pragma unroll
     for (int u = 0; u < SUB; ++u) {
       const int qrow = min(it.qw0 + 16 * u + lr, N - 1);
@@ -272,33 +287,55 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
 
   // Direct global->LDS loads of one key tile: each instruction moves 1 KB
   // (64 lanes x 16 B) to consecutive LDS; a lane fetches the global chunk
-  // that the swizzle assigns to its LDS position.
-  auto issue_tile = [&](uint16_t* dst, const Item& it, int kt) {
-    const int kb = kt * BN;
-    const uint16_t* K1 = (const uint16_t*)a.k1 + it.hrow * D;
-    const uint16_t* K2 = (const uint16_t*)a.k2 + it.hrow * D;
-    const uint16_t* V = (const uint16_t*)a.v + it.hrow * DV;
+  // that the swizzle assigns to its LDS position.  Segment i of this wave is
+  // one 1 KB piece of the K1 (sel 0), K2 (1) or V (2) tile; which piece, its
+  // LDS offset in a stage (wave-uniform), and the lane's byte offset inside
+  // the tile and key row (per lane) are the same for every tile.
+  constexpr int SPW = T::NSEG / T::WAVES;  // segments per wave
+  int seg_sel[SPW];
+  uint32_t seg_lds[SPW], seg_off[SPW];
+  int seg_row[SPW];
 #pragma unroll
-    for (int i = 0; i < T::NSEG / T::WAVES; ++i) {
-      const int seg = wave + i * T::WAVES;
-      const uint16_t* src;
-      uint16_t* ldst;
-      if (seg < 2 * KSEG) {
-        const int mtx = seg / KSEG, sg = seg % KSEG;
-        const int r = sg * (64 / NCH) + lane / NCH;
-        const int cch = T::kchunk(r, lane % NCH);
-        src = (mtx ? K2 : K1) + (size_t)min(kb + r, N - 1) * D + 8 * cch;
-        ldst = dst + mtx * KTILE + sg * 512;
-      } else {
-        // segment sg: keys 32*(sg % (BN/32)).. of channel block sg / (BN/32);
-        // lane: key +lane/2, channels +8*(lane&1)
-        const int sg = seg - 2 * KSEG;
-        const int cb = sg / (BN / 32);
-        const int r = 32 * (sg % (BN / 32)) + (lane >> 1);
-        src = V + (size_t)min(kb + r, N - 1) * DV + 16 * cb + 8 * (lane & 1);
-        ldst = dst + 2 * KTILE + sg * 512;
+  for (int i = 0; i < SPW; ++i) {
+    const int seg = wave + i * T::WAVES;
+    if (seg < 2 * KSEG) {
+      const int sg = seg % KSEG;
+      const int r = sg * (64 / NCH) + lane / NCH;
+      seg_sel[i] = seg / KSEG;
+      seg_lds[i] = 2u * (uint32_t)((seg / KSEG) * KTILE + sg * 512);
+      seg_row[i] = r;
+      seg_off[i] = 2u * (uint32_t)(r * D + 8 * T::kchunk(r, lane % NCH));
+    } else {
+      // segment sg: keys 32*(sg % (BN/32)).. of channel block sg / (BN/32);
+      // lane: key +lane/2, channels +8*(lane&1)
+      const int sg = seg - 2 * KSEG;
+      const int r = 32 * (sg % (BN / 32)) + (lane >> 1);
+      seg_sel[i] = 2;
+      seg_lds[i] = 2u * (uint32_t)(2 * KTILE + sg * 512);
+      seg_row[i] = r;
+      seg_off[i] = 2u * (uint32_t)(r * DV + 16 * (sg / (BN / 32)) + 8 * (lane & 1));
+    }
+  }
+  const uint32_t lds_stages = lds_offset(stages);  // LDS byte address of the ring
+  auto issue_tile = [&](int buf, const Item& it, int kt) {
+    const int kb = kt * BN;
+    const size_t row0 = head_row(it) + (size_t)kb;
+    const char* bk1 = (const char*)a.k1 + row0 * (2 * D);
+    const char* bk2 = (const char*)a.k2 + row0 * (2 * D);
+    const char* bv = (const char*)a.v + row0 * (2 * DV);
+    const uint32_t lds0 = lds_stages + (uint32_t)(buf * T::STAGE * 2);
+    if (kb + BN <= N) {
+#pragma unroll
+      for (int i = 0; i < SPW; ++i)
+        lds_dma16_s(seg_sel[i] == 0 ? bk1 : (seg_sel[i] == 1 ? bk2 : bv), seg_off[i], lds0 + seg_lds[i]);
+    } else {
+      // ragged last tile: rows past N - 1 read row N - 1 instead
+#pragma unroll
+      for (int i = 0; i < SPW; ++i) {
+        const uint32_t row_bytes = seg_sel[i] == 2 ? 2 * DV : 2 * D;
+        const uint32_t off = seg_off[i] - (uint32_t)max(0, kb + seg_row[i] - (N - 1)) * row_bytes;
+        lds_dma16_s(seg_sel[i] == 0 ? bk1 : (seg_sel[i] == 1 ? bk2 : bv), off, lds0 + seg_lds[i]);
       }
-      lds_dma16(src, lds_offset(ldst));
     }
   };
 
@@ -307,16 +344,24 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
   const u32x4 ones_u = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
   const bf16x8 ones = as_bf16x8(ones_u);
 
-  // One key tile.  MASK: the tile holds keys past some row's diagonal or
-  // past N; those tiles take a separate instantiation so that the common
-  // unmasked tiles carry no per-element compare/select work.
-  auto tile_body = [&](const uint16_t* stg, int kb, int qw0, auto mask_tag) {
+  using Scores = float[SUB][4 * NB];  // this lane's raw scores of one tile
+  using PFrags = bf16x8[NC][SUB];      // P^T fragments of one tile
+
+  // S^T = K Q^T for both sub-tiles; block b of sc holds keys 16b+4lg+j.
+  // MASK: the tile holds keys past some row's diagonal or past N; those
+  // tiles take a separate instantiation so that the common unmasked tiles
+  // carry no per-element compare/select work.
+  auto qk = [&](Scores& sc, const uint16_t* stg, int kb, int qw0, auto mask_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const uint16_t* ks_ = stg + mp * KTILE;
-    const uint16_t* vs = stg + 2 * KTILE;
-
-    // S^T = K Q^T for both sub-tiles; block b holds keys 16b+4lg+j
-    float s[SUB][4 * NB];
+    // key 16b+4lg+j of the tile is visible to sub-tile u's query iff
+    // 16b+j <= lim[u] (a compile-time constant against one register)
+    int lim[SUB];
+#pragma unroll
+    for (int u = 0; u < SUB; ++u) {
+      const int last_key = CAUSAL ? min(qw0 + 16 * u + lr, N - 1) : N - 1;
+      lim[u] = last_key - kb - 4 * lg;
+    }
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const int kr = 16 * b + lr;
@@ -335,62 +380,71 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           float x = acc[u][j];
-          if (MASK) {
-            const int kabs = kb + 16 * b + 4 * lg + j;
-            const int qabs = qw0 + 16 * u + lr;
-            x = ((kabs < N) && (!CAUSAL || kabs <= qabs)) ? x : -INFINITY;
-          }
-          s[u][4 * b + j] = x;
+          if (MASK) x = (16 * b + j <= lim[u]) ? x : -INFINITY;
+          sc[u][4 * b + j] = x;
         }
     }
+  };
 
-    // running maxima: one rescale branch per tile for both sub-tiles
-    {
-      float mt[SUB];
-      bool need = false;
+  // running maxima: the tile's row maxima (log2 units) and whether any row
+  // of the wave needs a new reference; then one rescale branch per tile for
+  // both sub-tiles
+  auto tile_max = [&](const Scores& sc, float (&mt)[SUB]) {
+    bool need = false;
+#pragma unroll
+    for (int u = 0; u < SUB; ++u) {
+      float x = sc[u][0];
+#pragma unroll
+      for (int i = 1; i < 4 * NB; ++i) x = fmaxf(x, sc[u][i]);
+      mt[u] = max4_groups(x) * c;
+      need |= mt[u] > m[u] + kRescaleThreshold;
+    }
+    return need;
+  };
+  auto rescale = [&](const float (&mt)[SUB], bool need) {
+    if (wave_any(need)) {
 #pragma unroll
       for (int u = 0; u < SUB; ++u) {
-        float x = s[u][0];
+        const float mn = fmaxf(m[u], mt[u]);
+        const float alpha = (mn == -INFINITY) ? 1.0f : exp2_fast(m[u] - mn);
+        m[u] = mn;
+        L[u] *= alpha;
 #pragma unroll
-        for (int i = 1; i < 4 * NB; ++i) x = fmaxf(x, s[u][i]);
-        mt[u] = max4_groups(x) * c;
-        need |= mt[u] > m[u] + kRescaleThreshold;
+        for (int cb = 0; cb < CB; ++cb) O[u][cb] *= alpha;
       }
-      if (wave_any(need)) {
+    }
+  };
+  auto update_max = [&](const Scores& sc) {
+    float mt[SUB];
+    const bool need = tile_max(sc, mt);
+    rescale(mt, need);
+  };
+
+  // P^T = exp2(S^T c - m) rounded to bf16; chunk cc = blocks 2cc (e 0..3)
+  // and 2cc+1 (e 4..7); the row sums of the rounded P go into L
+  auto make_p = [&](const Scores& sc, PFrags& pf) {
 #pragma unroll
-        for (int u = 0; u < SUB; ++u) {
-          const float mn = fmaxf(m[u], mt[u]);
-          const float alpha = (mn == -INFINITY) ? 1.0f : exp2_fast(m[u] - mn);
-          m[u] = mn;
-          L[u] *= alpha;
-#pragma unroll
-          for (int cb = 0; cb < CB; ++cb) O[u][cb] *= alpha;
-        }
-      }
+    for (int cc = 0; cc < NC; ++cc)
 #pragma unroll
       for (int u = 0; u < SUB; ++u) {
         const float nm = -m[u];
-#pragma unroll
-        for (int i = 0; i < 4 * NB; ++i) s[u][i] = exp2_fast(__builtin_fmaf(s[u][i], c, nm));
-      }
-    }
-
-    // O^T += V^T P^T: P^T fragment of chunk cc = blocks 2cc (e 0..3) and 2cc+1 (e 4..7)
-#pragma unroll
-    for (int cc = 0; cc < NC; ++cc) {
-      bf16x8 pf[SUB];
-#pragma unroll
-      for (int u = 0; u < SUB; ++u) {
         u32x4 pu;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const float* sp = &s[u][4 * (2 * cc + h)];
-          pu[2 * h] = pack_bf16x2(sp[0], sp[1]);
-          pu[2 * h + 1] = pack_bf16x2(sp[2], sp[3]);
+          const float* sp = &sc[u][4 * (2 * cc + h)];
+          pu[2 * h] = pack_bf16x2(exp2_fast(__builtin_fmaf(sp[0], c, nm)), exp2_fast(__builtin_fmaf(sp[1], c, nm)));
+          pu[2 * h + 1] = pack_bf16x2(exp2_fast(__builtin_fmaf(sp[2], c, nm)), exp2_fast(__builtin_fmaf(sp[3], c, nm)));
         }
-        pf[u] = as_bf16x8(pu);
-        L[u] = mfma16x16x32_bf16(ones, pf[u], L[u]);
+        pf[cc][u] = as_bf16x8(pu);
+        L[u] = mfma16x16x32_bf16(ones, pf[cc][u], L[u]);
       }
+  };
+
+  // O^T += V^T P^T
+  auto pv = [&](const uint16_t* stg, const PFrags& pf) {
+    const uint16_t* vs = stg + 2 * KTILE;
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
         u32x4 vu;
@@ -405,19 +459,197 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
         }
         const bf16x8 va = as_bf16x8(vu);
 #pragma unroll
-        for (int u = 0; u < SUB; ++u) O[u][cb] = mfma16x16x32_bf16(va, pf[u], O[u][cb]);
+        for (int u = 0; u < SUB; ++u) O[u][cb] = mfma16x16x32_bf16(va, pf[cc][u], O[u][cb]);
         // keep the scheduler from hoisting every V fragment read at once
         if (T::PV_FENCE > 0 && cb % T::PV_FENCE == T::PV_FENCE - 1) __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
+
+  // ---- pieces of the software-pipelined iteration (d <= 64) ----
+  // There a tile's scores are kept as t = s c - m (log2 units, -inf where
+  // masked): the row maxima are then taken over FMA results, which need no
+  // canonicalisation, and a rescale only shifts t.  Each group of
+  // instructions below ends in a scheduling fence, so that the matrix-core
+  // work of one tile and the VALU work of the other stay interleaved.
+
+  // K fragments (A operand) of 16-key block b
+  auto load_kf = [&](const uint16_t* ks_, int b, bf16x8 (&kf)[KS]) {
+    const int kr = 16 * b + lr;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int ch = 4 * ks + lg;
+      kf[ks] = as_bf16x8(ch < NCH ? ld16(ks_ + kr * D + 8 * T::kchunk(kr, ch)) : zero_u32x4());
+    }
+  };
+  // V^T fragment j = (32-key chunk j / CB, channel block j % CB)
+  auto load_vf = [&](const uint16_t* vs, int j) {
+    const int cc = j / CB, cb = j % CB;
+    u32x4 vu;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const u32x2 t2 = lds_read_tr16(vs + 16 * (BN * cb + 32 * cc + 16 * h) + 4 * lane);
+      vu[2 * h] = t2[0];
+      vu[2 * h + 1] = t2[1];
+    }
+    return as_bf16x8(vu);
+  };
+  // P^T chunk q = (32-key chunk q / SUB, sub-tile q % SUB) of the
+  // exponentiated tile e, rounded to bf16
+  auto pack_chunk = [&](const Scores& e, int q) {
+    const int cc = q / SUB, u = q % SUB;
+    u32x4 pu;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float* ep = &e[u][4 * (2 * cc + h)];
+      pu[2 * h] = pack_bf16x2(ep[0], ep[1]);
+      pu[2 * h + 1] = pack_bf16x2(ep[2], ep[3]);
+    }
+    return as_bf16x8(pu);
+  };
+  // P^T chunk q straight from t
+  auto p_chunk = [&](const Scores& t, int q) {
+    const int cc = q / SUB, u = q % SUB;
+    u32x4 pu;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float* tp = &t[u][4 * (2 * cc + h)];
+      pu[2 * h] = pack_bf16x2(exp2_fast(tp[0]), exp2_fast(tp[1]));
+      pu[2 * h + 1] = pack_bf16x2(exp2_fast(tp[2]), exp2_fast(tp[3]));
+    }
+    return as_bf16x8(pu);
+  };
+
+  // Phase A: S^T of the next tile (raw, into sn) from the K tile at ks_,
+  // block by block, each block with the exponentials of one block of the
+  // current tile (t -> 2^t in place).
+  auto phase_a = [&](const uint16_t* ks_, Scores& sn, Scores& t) {
+    bf16x8 kf[2][KS];
+    load_kf(ks_, 0, kf[0]);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (b + 1 < NB) load_kf(ks_, b + 1, kf[(b + 1) & 1]);
+      f32x4 acc[SUB];
+#pragma unroll
+      for (int u = 0; u < SUB; ++u) acc[u] = zero_f32x4();
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int u = 0; u < SUB; ++u) acc[u] = mfma16x16x32_bf16(kf[b & 1][ks], qf[u][ks], acc[u]);
+#pragma unroll
+      for (int u = 0; u < SUB; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sn[u][4 * b + j] = acc[u][j];
+#pragma unroll
+      for (int u = 0; u < SUB; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) t[u][4 * b + j] = exp2_fast(t[u][4 * b + j]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Phase B: P^T of the current tile (bf16, from the exponentials e) with
+  // its row sums, and O^T += V^T P^T (V tile at vs) fragment by fragment,
+  // each fragment with a slice of the next tile's t = s c - m (masked) and
+  // its row maxima.  Returns whether some row needs a new reference; mt
+  // gets the rows' maxima of t.
+  auto phase_b = [&](const uint16_t* vs, const Scores& e, Scores& sn, int kb, int qw0, float (&mt)[SUB],
+                     auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    int lim[SUB];
+#pragma unroll
+    for (int u = 0; u < SUB; ++u) {
+      const int last_key = CAUSAL ? min(qw0 + 16 * u + lr, N - 1) : N - 1;
+      lim[u] = last_key - kb - 4 * lg;
+    }
+    constexpr int J = NC * CB;
+    constexpr int NQ = NC * SUB;             // P chunks
+    constexpr int NV = SUB * 4 * NB;         // score values per lane
+    constexpr int PER = (NV + J - 1) / J;    // of them per group
+    static_assert(NQ - SUB <= CB, "later P chunks are packed before their PV products");
+    PFrags pf;
+    // chunks of the first 32 keys now; the others in the first groups
+#pragma unroll
+    for (int q = 0; q < SUB; ++q) pf[0][q] = pack_chunk(e, q);
+    float mx[SUB];
+#pragma unroll
+    for (int u = 0; u < SUB; ++u) mx[u] = -INFINITY;
+    bf16x8 vf[3];
+    vf[0] = load_vf(vs, 0);
+    if (J > 1) vf[1] = load_vf(vs, 1);
+#pragma unroll
+    for (int q = 0; q < SUB; ++q) L[q] = mfma16x16x32_bf16(ones, pf[0][q], L[q]);
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      if (j + 2 < J) vf[(j + 2) % 3] = load_vf(vs, j + 2);
+#pragma unroll
+      for (int u = 0; u < SUB; ++u) O[u][j % CB] = mfma16x16x32_bf16(vf[j % 3], pf[j / CB][u], O[u][j % CB]);
+      if (j >= 1 && j - 1 < NQ - SUB) {
+        const int q = SUB + j - 1;  // packed in the group before
+        L[q % SUB] = mfma16x16x32_bf16(ones, pf[q / SUB][q % SUB], L[q % SUB]);
+      }
+      if (j < NQ - SUB) {
+        const int q = SUB + j;
+        pf[q / SUB][q % SUB] = pack_chunk(e, q);
+      }
+#pragma unroll
+      for (int q = j * PER; q < (j + 1) * PER && q < NV; ++q) {
+        const int u = q / (4 * NB), i = q % (4 * NB);
+        float x = __builtin_fmaf(sn[u][i], c, -m[u]);
+        if (MASK) x = (16 * (i / 4) + (i % 4) <= lim[u]) ? x : -INFINITY;
+        sn[u][i] = x;
+        mx[u] = fmaxf(mx[u], x);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    bool need = false;
+#pragma unroll
+    for (int u = 0; u < SUB; ++u) {
+      mt[u] = max4_groups(mx[u]);
+      need |= mt[u] > kRescaleThreshold;
+    }
+    return need;
+  };
+  // raise the references of all rows whose t exceeds 0 (t, O, l follow)
+  auto rescale_t = [&](Scores& t, const float (&mt)[SUB], bool need) {
+    if (wave_any(need)) {
+#pragma unroll
+      for (int u = 0; u < SUB; ++u) {
+        const float dm = fmaxf(mt[u], 0.0f);
+        const float alpha = exp2_fast(-dm);
+        m[u] += dm;
+        L[u] *= alpha;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) O[u][cb] *= alpha;
+#pragma unroll
+        for (int i = 0; i < 4 * NB; ++i) t[u][i] -= dm;
+      }
+    }
+  };
+
+  // tile kt of the current item holds keys past a row's diagonal or past N
+  auto tile_masked = [&](const Item& it, int kb) {
+    return (CAUSAL && kb + BN - 1 > it.qw0) || (kb + BN > N);
+  };
+  // key tiles of the item that hold keys visible to this wave's rows
+  auto visible_tiles = [&](const Item& it) {
+    if (it.qw0 >= N) return 0;
+    return CAUSAL ? min(it.nkt, (it.qw0 + 16 * SUB - 1) / BN + 1) : it.nkt;
+  };
+
+  // One tile, phases in sequence.
   auto compute_tile = [&](const uint16_t* stg, const Item& it, int kt) {
     const int kb = kt * BN;
-    if (it.qw0 >= N || (CAUSAL && kb > it.qw0 + 16 * SUB - 1)) return;  // nothing visible for this wave
-    if ((CAUSAL && kb + BN - 1 > it.qw0) || (kb + BN > N))
-      tile_body(stg, kb, it.qw0, std::true_type{});
+    if (kt >= visible_tiles(it)) return;  // nothing visible for this wave
+    Scores sc;
+    PFrags pf;
+    if (tile_masked(it, kb))
+      qk(sc, stg, kb, it.qw0, std::true_type{});
     else
-      tile_body(stg, kb, it.qw0, std::false_type{});
+      qk(sc, stg, kb, it.qw0, std::false_type{});
+    update_max(sc);
+    make_p(sc, pf);
+    pv(stg, pf);
   };
 
   // map-1 wave: Y = O1/l1 - lambda O2/l2 with O2/l2 read from the exchange,
@@ -444,7 +676,7 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
       }
       const int row = it.qw0 + 16 * u + lr;
       if (row < N) {
-        uint16_t* __restrict__ Out = (uint16_t*)a.out + (it.hrow + row) * DV;
+        uint16_t* __restrict__ Out = (uint16_t*)a.out + (head_row(it) + row) * DV;
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
           float y[4];
@@ -486,23 +718,21 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
   };
 
   // The key tiles of all this workgroup's items form one stream through the
-  // ring of stage buffers; the load cursor runs STAGES-1 tiles ahead of the
-  // compute, across item boundaries.
+  // ring of stage buffers, across item boundaries; the load cursor runs one
+  // tile ahead of the tile last made available.
   struct Cursor {
     int r, kt;
     bool ok;
     Item it;
   };
-  int ib = 0;        // stage buffer of the next tile to load
-  int inflight = 0;  // tiles loaded or loading and not yet consumed
+  int ib = 0;  // stage buffer of the next tile to load
   auto load_next = [&](Cursor& q) {
     if (!q.ok) return;
-    issue_tile(stages + ib * T::STAGE, q.it, q.kt);
+    issue_tile(ib, q.it, q.kt);
     ib = ib + 1 == STAGES ? 0 : ib + 1;
-    ++inflight;
     if (++q.kt < q.it.nkt) return;
     q.kt = 0;
-    const long long i = item_at(++q.r);
+    const int i = item_at(++q.r);
     q.ok = i >= 0;
     if (q.ok) q.it = decode_item(i);
   };
@@ -518,17 +748,26 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
       for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qf[u][ks]));
   };
 
+  // Make the oldest loading tile available: this wave's loads have landed,
+  // the barrier extends that to everybody's and guarantees that nobody still
+  // reads the buffer the next load reuses.
+  auto avail = [&](Cursor& q) {
+    wait_vmem();
+    __syncthreads();
+    load_next(q);
+  };
+
   int r = 0;
-  const long long i0 = item_at(0);
+  const int i0 = item_at(0);
   if (i0 < 0) return;
   Item cur = decode_item(i0);
   Cursor ld{0, 0, true, cur};
   load_next(ld);
   load_q(cur);
   settle_q();
-#pragma unroll
-  for (int p = 1; p < STAGES - 1; ++p) load_next(ld);
-  int cbf = 0;  // stage buffer of the tile being consumed
+  int tb = 0;  // stage buffer of the current item's next tile to consume
+  auto next_buf = [&](int i) { return i + 1 == STAGES ? 0 : i + 1; };
+  Scores sA, sB;
   while (true) {
 #pragma unroll
     for (int u = 0; u < SUB; ++u) {
@@ -537,28 +776,91 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
       L[u] = zero_f32x4();
       m[u] = -INFINITY;
     }
-    for (int kt = 0; kt < cur.nkt; ++kt) {
-      // this wave's loads of tile kt have landed (a newer tile may still be
-      // loading: it is the newest vector-memory work of the wave)
-      if (STAGES > 2 && __builtin_amdgcn_readfirstlane(inflight) > 1)
-        wait_vmem_keep<T::NSEG / T::WAVES>();
-      else
-        wait_vmem();
-      __syncthreads();  // ... everybody's, and nobody still reads the buffer the next load reuses
-      // With three or more stages the load that follows an item's last tile
-      // waits until after the epilogue, so that it stays the newest.
-      if (STAGES == 2 || kt + 1 < cur.nkt) load_next(ld);
-      compute_tile(stages + cbf * T::STAGE, cur, kt);
-      --inflight;
-      cbf = cbf + 1 == STAGES ? 0 : cbf + 1;
+    if constexpr (T::PIPE) {
+      // Iteration kt forms P of tile kt (VALU) while the QK^T products of
+      // tile kt+1 run on the matrix cores, then runs PV of tile kt while the
+      // row maxima of tile kt+1 are taken.  Tiles kt and kt+1 are read
+      // together, so when tile t+1 becomes available tile t+2 loads into the
+      // third buffer (that of tile t-1, finished by everybody).
+      const int nvis = visible_tiles(cur);
+      // Every wave makes the same nkt calls of avail() per item (each holds
+      // a barrier): one for tile 0 here, then one at the start of step kt
+      // for tile kt+1, visible to this wave or not.
+      avail(ld);
+      // full step: P and PV of tile kt (t in sc) with S^T of tile kt+1 into
+      // sn, which leaves as t
+      auto full = [&](int kt, Scores& sc, Scores& sn, auto mask_tag) {
+        const uint16_t* bc = stages + tb * T::STAGE;
+        tb = next_buf(tb);
+        const uint16_t* bn = stages + tb * T::STAGE;
+        avail(ld);
+        float mt[SUB];
+        phase_a(bn + mp * KTILE, sn, sc);
+        const bool need = phase_b(bc + 2 * KTILE, sc, sn, (kt + 1) * BN, cur.qw0, mt, mask_tag);
+        rescale_t(sn, mt, need);
+      };
+      // last visible tile of this wave: P and PV only
+      auto last = [&](int kt, const Scores& t) {
+        const uint16_t* bc = stages + tb * T::STAGE;
+        tb = next_buf(tb);
+        if (kt + 1 < cur.nkt) avail(ld);
+        PFrags pf;
+#pragma unroll
+        for (int q = 0; q < NC * SUB; ++q) {
+          pf[q / SUB][q % SUB] = p_chunk(t, q);
+          L[q % SUB] = mfma16x16x32_bf16(ones, pf[q / SUB][q % SUB], L[q % SUB]);
+        }
+        pv(bc, pf);
+      };
+      // this wave's visible tiles: the first nfree carry no mask, the rest
+      // (the diagonal and the ragged end) do
+      const int nfree = min(nvis, min(CAUSAL ? (cur.qw0 + 1) / BN : N / BN, N / BN));
+      int kt = 0;
+      if (nvis > 0) {
+        // tile 0: scores, the first reference, then t
+        if (nfree == 0)
+          qk(sA, stages + tb * T::STAGE, 0, cur.qw0, std::true_type{});
+        else
+          qk(sA, stages + tb * T::STAGE, 0, cur.qw0, std::false_type{});
+        update_max(sA);
+#pragma unroll
+        for (int u = 0; u < SUB; ++u)
+#pragma unroll
+          for (int i = 0; i < 4 * NB; ++i) sA[u][i] = __builtin_fmaf(sA[u][i], c, -m[u]);
+        for (; kt + 1 < nfree; ++kt) {
+          full(kt, sA, sB, std::false_type{});
+#pragma unroll
+          for (int u = 0; u < SUB; ++u)
+#pragma unroll
+            for (int i = 0; i < 4 * NB; ++i) sA[u][i] = sB[u][i];
+        }
+        for (; kt + 1 < nvis; ++kt) {
+          full(kt, sA, sB, std::true_type{});
+#pragma unroll
+          for (int u = 0; u < SUB; ++u)
+#pragma unroll
+            for (int i = 0; i < 4 * NB; ++i) sA[u][i] = sB[u][i];
+        }
+        last(kt, sA);
+        ++kt;
+      }
+      for (; kt < cur.nkt; ++kt) {  // tiles no row of this wave sees
+        tb = next_buf(tb);
+        if (kt + 1 < cur.nkt) avail(ld);
+      }
+    } else {
+      for (int kt = 0; kt < cur.nkt; ++kt) {
+        avail(ld);
+        compute_tile(stages + tb * T::STAGE, cur, kt);
+        tb = next_buf(tb);
+      }
     }
-    const long long ni = item_at(r + 1);
+    const int ni = item_at(r + 1);
     const Item nxt = decode_item(ni < 0 ? i0 : ni);
     if (ni >= 0) load_q(nxt);  // the last tile's QK^T is done: qf is free
     __syncthreads();           // everybody is done with the last tile's buffer
-    epilogue(cur, stages + (cbf == 0 ? STAGES - 1 : cbf - 1) * T::STAGE);
+    epilogue(cur, stages + (tb == 0 ? STAGES - 1 : tb - 1) * T::STAGE);
     settle_q();
-    if (STAGES > 2) load_next(ld);
     if (ni < 0) break;
     cur = nxt;
     ++r;
