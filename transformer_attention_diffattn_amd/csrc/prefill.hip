@@ -247,9 +247,9 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
   const int G = gridDim.x, g = blockIdx.x, BH = a.BH;
   const int n_items = a.n_qtiles * BH;  // below 2^31 (checked by the host)
   auto item_at = [&](int r) -> int {
-    int pos = g;
-    if (r & 1) pos = (G % BH == 0) ? ((G / BH - 1 - g / BH) * BH + g % BH) : (G - 1 - g);
-    const int i = r * G + pos;
+    // integer division expands to vector code: keep the result scalar
+    const int alt = __builtin_amdgcn_readfirstlane((G % BH == 0) ? ((G / BH - 1 - g / BH) * BH + g % BH) : (G - 1 - g));
+    const int i = r * G + ((r & 1) ? alt : g);
     return i < n_items ? i : -1;
   };
 
@@ -637,18 +637,61 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
     return CAUSAL ? min(it.nkt, (it.qw0 + 16 * SUB - 1) / BN + 1) : it.nkt;
   };
 
-  // One tile, phases in sequence.
+  // t = s c - m of a whole raw tile (-inf where masked) and its row maxima;
+  // returns whether some row needs a new reference
+  auto scale_max = [&](Scores& sc, int kb, int qw0, float (&mt)[SUB], auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    bool need = false;
+#pragma unroll
+    for (int u = 0; u < SUB; ++u) {
+      const int last_key = CAUSAL ? min(qw0 + 16 * u + lr, N - 1) : N - 1;
+      const int lim = last_key - kb - 4 * lg;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4 * NB; ++i) {
+        float x = __builtin_fmaf(sc[u][i], c, -m[u]);
+        if (MASK) x = (16 * (i / 4) + (i % 4) <= lim) ? x : -INFINITY;
+        sc[u][i] = x;
+        mx = fmaxf(mx, x);
+      }
+      mt[u] = max4_groups(mx);
+      need |= mt[u] > kRescaleThreshold;
+    }
+    return need;
+  };
+
+  // One tile, phases in sequence.  The first tile of an item sets the
+  // references from its exact maxima; later ones work on t = s c - m.
   auto compute_tile = [&](const uint16_t* stg, const Item& it, int kt) {
     const int kb = kt * BN;
     if (kt >= visible_tiles(it)) return;  // nothing visible for this wave
     Scores sc;
     PFrags pf;
-    if (tile_masked(it, kb))
-      qk(sc, stg, kb, it.qw0, std::true_type{});
-    else
+    if (kt == 0) {
+      if (tile_masked(it, kb))
+        qk(sc, stg, kb, it.qw0, std::true_type{});
+      else
+        qk(sc, stg, kb, it.qw0, std::false_type{});
+      update_max(sc);
+#pragma unroll
+      for (int u = 0; u < SUB; ++u)
+#pragma unroll
+        for (int i = 0; i < 4 * NB; ++i) sc[u][i] = __builtin_fmaf(sc[u][i], c, -m[u]);
+    } else {
       qk(sc, stg, kb, it.qw0, std::false_type{});
-    update_max(sc);
-    make_p(sc, pf);
+      float mt[SUB];
+      bool need;
+      if (tile_masked(it, kb))
+        need = scale_max(sc, kb, it.qw0, mt, std::true_type{});
+      else
+        need = scale_max(sc, kb, it.qw0, mt, std::false_type{});
+      rescale_t(sc, mt, need);
+    }
+#pragma unroll
+    for (int q = 0; q < NC * SUB; ++q) {
+      pf[q / SUB][q % SUB] = p_chunk(sc, q);
+      L[q % SUB] = mfma16x16x32_bf16(ones, pf[q / SUB][q % SUB], L[q % SUB]);
+    }
     pv(stg, pf);
   };
 
@@ -732,7 +775,7 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
     ib = ib + 1 == STAGES ? 0 : ib + 1;
     if (++q.kt < q.it.nkt) return;
     q.kt = 0;
-    const int i = item_at(++q.r);
+    const int i = __builtin_amdgcn_readfirstlane(item_at(++q.r));
     q.ok = i >= 0;
     if (q.ok) q.it = decode_item(i);
   };
