@@ -110,9 +110,10 @@ struct Bf16Cfg {
   static constexpr int SUB = 2;
   static constexpr int BN = D >= 128 ? 32 : 64;  // d = 128: keeps a wave within 256 registers
   // Software-pipelined tile loop (QK^T of the next tile overlaps the
-  // softmax of the current one); d = 128 has no registers to spare for the
-  // second tile's scores and runs the phases of a tile in sequence.
-  static constexpr bool PIPE = D <= 64;
+  // softmax of the current one); the sequential tile body stays as the
+  // alternative for shapes whose second score tile would not fit in
+  // registers.
+  static constexpr bool PIPE = D <= 128;
   static constexpr int STAGES = PIPE ? 3 : 2;  // LDS stage buffers
   static constexpr int PV_FENCE = D >= 128 ? 4 : 0;  // channel blocks between scheduling fences
 };
