@@ -9,7 +9,10 @@ the prefill kernel's roofline fraction against the bf16 dense MFMA peak, the
 CPU fp64 oracle timed on a bounded sample of the same workload, and a decode
 leg (diffattn_decode on 64 sequences x 16 heads x 32768 cached keys, d=128)
 reported in HBM GB/s against the 8 TB/s peak.  Inputs are seeded synthetic
-tensors already resident in HBM when timing starts.
+tensors already resident in HBM when timing starts.  The prefill step is
+replayed from a HIP graph (checked equal to the eager step) so that host
+launch overhead does not idle the GPU; kernel durations come from HIP events
+on the stream the kernels run on.
 """
 
 from __future__ import annotations
@@ -49,19 +52,33 @@ def _traffic(kind: str, src: str):
     return t.get("bytes_per_launch") if t.get("source_sha256_16") == _src_hash(src) else None
 
 
-def _timed_loop(fn, steps, stream, torch):
-    """Run fn() `steps` times; returns (total ms, list of per-launch ms of the
-    event pair fn brackets itself with)."""
-    per = []
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
+def _graph(fn, torch):
+    """Capture fn (library launches on torch's current stream) into a HIP
+    graph after one eager warm-up call on a side stream."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
     torch.cuda.synchronize()
-    t0.record(stream)
-    for _ in range(steps):
-        per.append(fn())
-    t1.record(stream)
+    return g
+
+
+def _timed(replay, n, stream, torch):
+    """Milliseconds for n back-to-back calls of replay(), from HIP events on
+    the stream the work runs on."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    return t0.elapsed_time(t1), [a.elapsed_time(b) for a, b in per]
+    e0.record(stream)
+    for _ in range(n):
+        replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1)
 
 
 def cpu_baseline(x, w, budget_s: float):
@@ -94,7 +111,7 @@ def cpu_baseline(x, w, budget_s: float):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--decode-steps", type=int, default=10)
     ap.add_argument("--no-decode", action="store_true", help="skip the decode leg")
@@ -126,21 +143,28 @@ def main():
 
     def step():
         da.lam(x["lq1"], x["lk1"], x["lq2"], x["lk2"], x["lambda_init"], out=lam_t)
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
+        fwd()
+
+    def fwd():
         da.fwd(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam_t, x["lambda_init"], eps=x["eps"],
                causal=w.causal, out=out)
-        e1.record(stream)
-        return e0, e1
 
+    # The step is replayed from a HIP graph so that the host's per-call
+    # overhead does not leave the GPU idle between launches; the graph holds
+    # exactly the eager step's two library launches.
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    g_step = _graph(step, torch)
+    g_fwd = _graph(fwd, torch)
     for _ in range(args.warmup):
-        step()
-    total_ms, per = _timed_loop(step, args.steps, stream, torch)
-    if not torch.isfinite(out.float()).all():
-        raise RuntimeError("non-finite prefill output")
+        g_step.replay()
+    total_ms = _timed(g_step.replay, args.steps, stream, torch)
+    if not torch.equal(out, eager):
+        raise RuntimeError("graph replay of the step differs from the eager step")
+    # the dominant kernel alone, same launch configuration
+    kern_ms = _timed(g_fwd.replay, args.steps, stream, torch) / args.steps
     ms_step = total_ms / args.steps
-    kern_ms = sum(per) / len(per)
     flops = 12.0 * w.d * w.pairs() * w.B * w.H
     value = flops / (ms_step * 1e-3) / 1e12
     achieved = flops / (kern_ms * 1e-3) / 1e12
@@ -169,23 +193,18 @@ def main():
         outd = torch.empty((wd.B, wd.H, 1, 2 * wd.d), dtype=torch.bfloat16, device=dev)
 
         def dstep():
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
             da.decode(y["q1"], y["q2"], y["k1c"], y["k2c"], y["vc"], lam_d, y["lambda_init"],
                       cache_len=y["cache_len"], eps=y["eps"], workspace=ws, out=outd)
-            e1.record(stream)
-            return e0, e1
 
         for _ in range(2):
             dstep()
-        dtotal, dper = _timed_loop(dstep, args.decode_steps, stream, torch)
-        dms = sum(dper) / len(dper)
+        dtotal = _timed(dstep, args.decode_steps, stream, torch)
+        dms = dtotal / args.decode_steps
         nbytes = wd.B * wd.H * wd.N * 8 * wd.d  # K1 + K2 + V per cached key, bf16
         gbs = nbytes / (dms * 1e-3) / 1e9
         res["decode"] = {
             "workload": wd.name, "B": wd.B, "H": wd.H, "L": wd.N, "d": wd.d,
-            "ms_per_step": round(dtotal / args.decode_steps, 4),
+            "ms_per_step": round(dms, 4),
             "roofline": {"bound": "hbm", "kernel": "decode_split_kernel<bf16,128> + decode_merge_kernel",
                          "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4),

@@ -13,10 +13,10 @@
 // reference maximum m, denominator l, numerator O[2d]); the V tile staged in
 // LDS feeds both maps' PV products (A1 V - lambda A2 V = (A1 - lambda A2) V).
 //
-// Layout of the work (bf16 kernel): a workgroup owns BM = 128 query rows of
-// one head (8 waves x 16 rows) and streams BN-key tiles of K1, K2, V through
-// double-buffered LDS.  Products are computed transposed so that every
-// per-row quantity lives in the lane of its query:
+// Layout of the work (bf16 kernel): a workgroup takes (128 query rows, head)
+// items in turn (8 waves, 32 rows and one map each) and streams BN-key tiles
+// of K1, K2, V through a ring of LDS stage buffers.  Products are computed
+// transposed so that every per-row quantity lives in the lane of its query:
 //   S^T = K Q^T   (16x16x32 bf16 MFMA, A = K rows from LDS, B = Q^T in VGPRs)
 //   O^T += V^T P^T (A = V^T from LDS, B = P^T built in-lane from S^T)
 //   l   += 1^T P^T (the same MFMA with A = ones: row sums of the rounded P)
@@ -90,13 +90,13 @@ __device__ __forceinline__ void epilogue_values(const f32x4 (&O1)[CB], const f32
 // ---------------------------------------------------------------------------
 // bf16 kernel
 //
-// A workgroup owns BM = 128 query rows of one head and runs 8 waves: wave w
-// computes map (w & 1) for the 32 rows of row group (w >> 1), as two 16-row
-// sub-tiles so that each K or V fragment read from LDS feeds two MFMAs.  The
-// two maps of a row group only meet in the epilogue, where the map-2 wave
-// hands O2/l2 to the map-1 wave through LDS.  K1, K2 and V tiles of BN keys
-// arrive by direct global->LDS loads into two stage buffers (the next tile
-// loads while the current one is consumed).  Rows are XOR-swizzled in 16-byte
+// A work item is BM = 128 query rows of one head; a workgroup runs 8 waves:
+// wave w computes map (w & 1) for the 32 rows of row group (w >> 1), as two
+// 16-row sub-tiles so that each K or V fragment read from LDS feeds two
+// MFMAs.  The two maps of a row group only meet in the epilogue, where the
+// map-2 wave hands O2/l2 to the map-1 wave through LDS.  K1, K2 and V tiles
+// of BN keys arrive by direct global->LDS loads into a ring of stage buffers
+// (later tiles load while earlier ones are consumed).  Rows are XOR-swizzled in 16-byte
 // chunks so that K fragment reads are free of bank conflicts.  A V tile is
 // stored as [16-channel block][key][16 channels]: the transposing LDS read
 // (ds_read_b64_tr_b16) of a V^T fragment then covers 512 contiguous bytes,
@@ -1111,15 +1111,29 @@ int prefill_block_threads(bool bf16, int d) {
   }
 }
 
+// Compute units of the current device, queried once per device.
+static hipError_t compute_units(int* ncu) {
+  static int cache[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < 64 && cache[dev] > 0) {
+    *ncu = cache[dev];
+    return hipSuccess;
+  }
+  e = hipDeviceGetAttribute(ncu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess && dev >= 0 && dev < 64) cache[dev] = *ncu;
+  return e;
+}
+
 template <int D, bool C, bool NM>
 static hipError_t launch_one(bool bf16, const PrefillArgs& a, hipStream_t s) {
   const long long items = (long long)a.n_qtiles * (long long)a.BH;
   const dim3 block(prefill_block_threads(bf16, D));
   if (bf16) {
     // persistent: one workgroup per compute unit walks the item list
-    int dev = 0, ncu = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    int ncu = 0;
+    const hipError_t e = compute_units(&ncu);
     if (e != hipSuccess) return e;
     const long long grid = items < ncu ? items : (ncu > 0 ? ncu : 1);
     hipLaunchKernelGGL((prefill_bf16_kernel<D, C, NM>), dim3((unsigned)grid), block, 0, s, a);
