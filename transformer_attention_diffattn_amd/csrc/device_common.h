@@ -24,6 +24,16 @@ constexpr float kLog2e = 1.44269504088896340736f;
 // numerator and denominator always share the same reference.
 constexpr float kRescaleThreshold = 8.0f;
 
+// Fourth word of a buffer resource for raw (byte-offset) access: 32-bit data
+// format, no swizzle; with stride 0 the hardware drops every access whose
+// offset + size exceeds the resource's byte count.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
+// Cache-policy operand of a store written once and not read again by the
+// kernel (the non-temporal bit): the lines should not displace K/V tiles
+// that other workgroups still read from the L2.
+constexpr int kStoreStreaming = 2;
+
 __device__ __forceinline__ f32x4 mfma16x16x32_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }

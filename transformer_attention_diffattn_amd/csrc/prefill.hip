@@ -127,7 +127,7 @@ struct Bf16Tile {
   static constexpr int BN = Bf16Cfg<D>::BN;
   static constexpr int STAGES = Bf16Cfg<D>::STAGES;
   static constexpr bool PIPE = Bf16Cfg<D>::PIPE;
-  static_assert(STAGES == (PIPE ? 3 : 2), "stage ring of the tile loop");
+  static_assert(STAGES >= (PIPE ? 3 : 2), "stage ring of the tile loop");
   static constexpr int PV_FENCE = Bf16Cfg<D>::PV_FENCE;
   static constexpr int KS = (D + 31) / 32;  // 32-wide k-steps of the QK^T MFMA
   static constexpr int NB = BN / 16;        // 16-key score blocks per tile
@@ -226,6 +226,8 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
   constexpr int STAGES = T::STAGES;
   __shared__ __attribute__((aligned(16))) uint16_t stages[STAGES * T::STAGE];
   __shared__ float wsh[DV];  // norm weight
+  __shared__ float ssx[T::WAVES][T::SUB * 16];  // epilogue: half-row sums of squares
+  __shared__ float dnx[T::WAVES][T::SUB * 16];  // epilogue: per-row scales
 
   const int lane = threadIdx.x & 63;
   // wave-uniform values live in scalar registers
@@ -696,69 +698,121 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
     pv(stg, pf);
   };
 
-  // map-1 wave: Y = O1/l1 - lambda O2/l2 with O2/l2 read from the exchange,
-  // then the norm, the scale and the store
-  auto finish_rows = [&](const Item& it, const float* xch) {
+  // Epilogue of one item.  The two waves of a row group (one per map) each
+  // finish half of the channels: a wave sends the other half of its
+  // accumulators and its per-row scale (1/l1, or lambda/l2 for map 2)
+  // through LDS, receives its partner's part of its own half, forms
+  // Y = O1/l1 - lambda O2/l2 there, and the two halves' sums of squares meet
+  // through a small LDS array for the RMSNorm.  The exchange uses the stage
+  // buffers that no load targets during the epilogue (all but the one
+  // receiving the next item's first tile), for all row groups at once and
+  // UR sub-tiles per round.  The next item's Q rows are loaded once the
+  // first round's sent halves have left the registers.
+  constexpr int HC = CB / 2;                  // channel blocks per half
+  constexpr int LPR = DV / 16;                // output store lanes per row (16 bytes each)
+  constexpr int RPI = 64 / LPR;               // rows per store instruction
+  constexpr int XS = HC * 4 * 64;             // floats one wave sends per sub-tile
+  constexpr int XU = 2 * XS;                  // floats per row group and sub-tile
+  constexpr int CAP = (STAGES - 1) * T::STAGE / 2;  // floats in the free buffers
+  constexpr int UR_FIT = CAP / (RG * XU);
+  constexpr int UR = UR_FIT >= SUB ? SUB : UR_FIT;  // sub-tiles per round
+  constexpr int RPB = (T::STAGE / 2) / (UR * XU);   // row groups per stage buffer
+  static_assert(CB % 2 == 0 && UR >= 1 && SUB % UR == 0 && RPB >= 1 && RG <= RPB * (STAGES - 1),
+                "epilogue exchange");
+  constexpr int EPI_STORES = (SUB / UR) * (16 * UR / RPI);  // vector-memory stores per wave
+  // The next item's Q rows load during the epilogue where registers allow
+  // (d <= 64); otherwise after it, their latency exposed once per item.
+  constexpr bool EARLY_Q = D <= 64;
+  auto epilogue_map = [&](const Item& it, int nb, int ni, const Item& nxt, auto map_tag) {
+    constexpr int MP = decltype(map_tag)::value;          // this wave's map
+    constexpr int own0 = MP * HC, send0 = (1 - MP) * HC;  // first channel block of each half
+    // lane indices re-derived from an opaque copy of the lane id, so that the
+    // epilogue's lane-dependent addresses are formed here rather than kept
+    // in registers through the tile loop
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int lr = ln & 15, lg = ln >> 4;
+    // nb: the buffer of the next tile to consume (the next item's first)
+    const int fb0 = nb == 0 ? STAGES - 1 : nb - 1;  // the buffer the last tile used
+    const int fb1 = fb0 == 0 ? STAGES - 1 : fb0 - 1;
+    float* region = (float*)(stages + (rg / RPB == 0 ? fb0 : fb1) * T::STAGE) + (rg % RPB) * UR * XU;
+    float* sent = region + MP * UR * XS;
+    const float* recv = region + (1 - MP) * UR * XS;
+    // waves whose rows all lie past N run the exchange too (no store
+    // follows), so the accumulators are updated on one path only
+    float dn[SUB];
 #pragma unroll
-    for (int u = 0; u < SUB; ++u) {
-      // O becomes Y in place: one pass over the exchange, no second copy
-      const float i1 = 1.0f / L[u][0];
-      float ss = 0.f;
+    for (int u = 0; u < SUB; ++u) dn[u] = (MP ? lam : 1.0f) / L[u][0];
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        const f32x4 o2 = *reinterpret_cast<const f32x4*>(xch + ((u * CB + cb) * 64 + lane) * 4);
+    for (int u0 = 0; u0 < SUB; u0 += UR) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          O[u][cb][j] = O[u][cb][j] * i1 - lam * o2[j];
-          ss += O[u][cb][j] * O[u][cb][j];
+      for (int v = 0; v < UR; ++v) {
+#pragma unroll
+        for (int h = 0; h < HC; ++h)
+          *reinterpret_cast<f32x4*>(sent + ((v * HC + h) * 64 + ln) * 4) = O[u0 + v][send0 + h];
+        if (lg == 0) dnx[wave][16 * (u0 + v) + lr] = dn[u0 + v];
+      }
+      __syncthreads();
+      if (EARLY_Q && u0 == 0 && ni >= 0) load_q(nxt);  // qf is free since the last tile's QK^T
+      float ssp[UR];
+#pragma unroll
+      for (int v = 0; v < UR; ++v) {
+        const int u = u0 + v;
+        float ss = 0.f;
+        const float dp = dnx[wave ^ 1][16 * u + lr];  // the partner's scale
+#pragma unroll
+        for (int h = 0; h < HC; ++h) {
+          const f32x4 o = *reinterpret_cast<const f32x4*>(recv + ((v * HC + h) * 64 + ln) * 4);
+          const f32x4 y = MP ? o * dp - O[u][own0 + h] * dn[u] : O[u][own0 + h] * dn[u] - o * dp;
+          O[u][own0 + h] = y;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) ss += y[j] * y[j];
         }
+        ssp[v] = sum_over_lane_groups(ss);
+        if (NORM && lg == 0) ssx[wave][16 * u + lr] = ssp[v];
       }
-      float r = 1.0f;
-      if (NORM) {
-        ss = sum_over_lane_groups(ss);
-        r = a.out_scale / sqrtf(ss * (1.0f / DV) + a.eps);
-      }
-      const int row = it.qw0 + 16 * u + lr;
-      if (row < N) {
-        uint16_t* __restrict__ Out = (uint16_t*)a.out + (head_row(it) + row) * DV;
+      // the partner's sum of squares; also the last read of this round's region
+      __syncthreads();
+      // Y of this wave's half, bf16, staged row-major in its half of the
+      // region (everybody's reads of it are done) and stored as whole row
+      // segments: DV bytes per row, 16 bytes per lane.
+      uint16_t* stg = (uint16_t*)(region + MP * UR * XS);
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
+      for (int v = 0; v < UR; ++v) {
+        const int u = u0 + v;
+        float r = 1.0f;
+        if (NORM) r = a.out_scale / sqrtf((ssp[v] + ssx[wave ^ 1][16 * u + lr]) * (1.0f / DV) + a.eps);
+#pragma unroll
+        for (int h = 0; h < HC; ++h) {
+          const int cb = own0 + h;
           float y[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) y[j] = O[u][cb][j] * (NORM ? r * wsh[16 * cb + 4 * lg + j] : 1.0f);
           u32x2 pk = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
-          *reinterpret_cast<u32x2*>(Out + 16 * cb + 4 * lg) = pk;
+          *reinterpret_cast<u32x2*>(stg + (16 * v + lr) * (DV / 2) + 16 * h + 4 * lg) = pk;
         }
       }
+      // Buffer stores against the head's N output rows: rows past N are
+      // dropped by the hardware's range check, so every wave issues the
+      // same EPI_STORES stores and no branch hides them from the counters.
+      const __amdgpu_buffer_rsrc_t ob = __builtin_amdgcn_make_buffer_rsrc(
+          (uint16_t*)a.out + head_row(it) * DV, 0, N * DV * 2, kBufferRsrcWord3);
+#pragma unroll
+      for (int q = 0; q < 16 * UR / RPI; ++q) {
+        const int rr = q * RPI + ln / LPR;  // row within the round: 16 v + lr
+        const int row = it.qw0 + 16 * (u0 + rr / 16) + rr % 16;
+        const u32x4 val = *reinterpret_cast<const u32x4*>(stg + rr * (DV / 2) + 8 * (ln % LPR));
+        __builtin_amdgcn_raw_buffer_store_b128(val, ob, (row * DV + 16 * own0 + 8 * (ln % LPR)) * 2, 0, kStoreStreaming);
+      }
+      // the region is reused by the next round's sends
+      if (u0 + UR < SUB) __syncthreads();
     }
   };
-
-  // Epilogue of one item in stage buffer `xb` (the one its last tile used;
-  // no load targets it before the epilogue ends): the map-2 wave of each row
-  // group publishes O2/l2 (fp32, in its lane layout), the map-1 wave forms
-  // Y = O1/l1 - lambda O2/l2, normalises and stores; XR row groups per phase.
-  constexpr int XW = 16 * SUB * DV;                  // floats per row group
-  constexpr int XR_FIT = (T::STAGE * 2) / (XW * 4);  // row groups per stage buffer
-  constexpr int XR = XR_FIT >= RG ? RG : XR_FIT;
-  static_assert(XR >= 1 && RG % XR == 0, "exchange phases");
-  auto epilogue = [&](const Item& it, uint16_t* xb) {
-    float* xch = (float*)xb + (rg % XR) * XW;
-#pragma unroll
-    for (int ph = 0; ph < RG / XR; ++ph) {
-      const bool mine = rg / XR == ph;
-      if (mine && mp == 1 && it.qw0 < N) {
-#pragma unroll
-        for (int u = 0; u < SUB; ++u) {
-          const float il = 1.0f / L[u][0];
-#pragma unroll
-          for (int cb = 0; cb < CB; ++cb)
-            *reinterpret_cast<f32x4*>(xch + ((u * CB + cb) * 64 + lane) * 4) = O[u][cb] * il;
-        }
-      }
-      __syncthreads();
-      if (mine && mp == 0 && it.qw0 < N) finish_rows(it, xch);
-      __syncthreads();
-    }
+  auto epilogue = [&](const Item& it, int nb, int ni, const Item& nxt) {
+    if (mp)
+      epilogue_map(it, nb, ni, nxt, std::integral_constant<int, 1>{});
+    else
+      epilogue_map(it, nb, ni, nxt, std::integral_constant<int, 0>{});
   };
 
   // The key tiles of all this workgroup's items form one stream through the
@@ -769,11 +823,16 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
     bool ok;
     Item it;
   };
-  int ib = 0;  // stage buffer of the next tile to load
+  // Tiles loading ahead of the one made available next: the pipelined loop
+  // reads two tiles at a time, so one buffer fewer is free for loads.
+  constexpr int LOOK = T::PIPE ? STAGES - 2 : STAGES - 1;
+  int ib = 0;       // stage buffer of the next tile to load
+  int pending = 0;  // tiles loading and not yet made available
   auto load_next = [&](Cursor& q) {
     if (!q.ok) return;
     issue_tile(ib, q.it, q.kt);
     ib = ib + 1 == STAGES ? 0 : ib + 1;
+    ++pending;
     if (++q.kt < q.it.nkt) return;
     q.kt = 0;
     const int i = __builtin_amdgcn_readfirstlane(item_at(++q.r));
@@ -792,11 +851,24 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
       for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qf[u][ks]));
   };
 
-  // Make the oldest loading tile available: this wave's loads have landed,
-  // the barrier extends that to everybody's and guarantees that nobody still
-  // reads the buffer the next load reuses.
+  // Make the oldest loading tile available: this wave's loads of it have
+  // landed (those of a newer tile, the wave's newest vector-memory work, may
+  // still be in flight), the barrier extends that to everybody's and
+  // guarantees that nobody still reads the buffer the next load reuses.
+  // after an epilogue its output stores are the wave's newest vector-memory
+  // work: the tile (and Q rows) issued before them may be waited for alone
+  bool after_epilogue = false;
   auto avail = [&](Cursor& q) {
-    wait_vmem();
+    if (after_epilogue) {
+      static_assert(LOOK == 1, "after an epilogue only the tile being made available is loading");
+      wait_vmem_keep<EPI_STORES>();
+      after_epilogue = false;
+    } else if (LOOK > 1 && __builtin_amdgcn_readfirstlane(pending) > 1) {
+      wait_vmem_keep<SPW>();
+    } else {
+      wait_vmem();
+    }
+    --pending;
     __syncthreads();
     load_next(q);
   };
@@ -809,6 +881,8 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
   load_next(ld);
   load_q(cur);
   settle_q();
+#pragma unroll
+  for (int p = 1; p < LOOK; ++p) load_next(ld);
   int tb = 0;  // stage buffer of the current item's next tile to consume
   auto next_buf = [&](int i) { return i + 1 == STAGES ? 0 : i + 1; };
   Scores sA, sB;
@@ -901,9 +975,10 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
     }
     const int ni = item_at(r + 1);
     const Item nxt = decode_item(ni < 0 ? i0 : ni);
-    if (ni >= 0) load_q(nxt);  // the last tile's QK^T is done: qf is free
-    __syncthreads();           // everybody is done with the last tile's buffer
-    epilogue(cur, stages + (tb == 0 ? STAGES - 1 : tb - 1) * T::STAGE);
+    __syncthreads();  // everybody is done with the last tiles' buffers
+    epilogue(cur, tb, ni, nxt);
+    if (!EARLY_Q && ni >= 0) load_q(nxt);
+    after_epilogue = EARLY_Q;
     settle_q();
     if (ni < 0) break;
     cur = nxt;
