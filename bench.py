@@ -173,6 +173,8 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
+        # the same step priced at Eq. 1's 8 d flops per pair (two PV products only)
+        "eq1_tflops": round(value * 8.0 / 12.0, 2),
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "v_width": 2 * w.d,
                    "causal": w.causal, "lambda_init": x["lambda_init"],
                    "flops_per_pair": 12 * w.d, "pairs_per_head": w.pairs()},

@@ -116,6 +116,9 @@ struct Bf16Cfg {
   static constexpr bool PIPE = D <= 128;
   static constexpr int STAGES = PIPE ? 3 : 2;  // LDS stage buffers
   static constexpr int PV_FENCE = D >= 128 ? 4 : 0;  // channel blocks between scheduling fences
+  // LDS fragment reads issued ahead of their MFMAs in the pipelined loop
+  static constexpr int K_AHEAD = 1;  // 16-key blocks of K
+  static constexpr int V_AHEAD = 2;  // V^T fragments
 };
 
 template <int D>
@@ -127,6 +130,8 @@ struct Bf16Tile {
   static constexpr int BN = Bf16Cfg<D>::BN;
   static constexpr int STAGES = Bf16Cfg<D>::STAGES;
   static constexpr bool PIPE = Bf16Cfg<D>::PIPE;
+  static constexpr int K_AHEAD = Bf16Cfg<D>::K_AHEAD;
+  static constexpr int V_AHEAD = Bf16Cfg<D>::V_AHEAD;
   static_assert(STAGES >= (PIPE ? 3 : 2), "stage ring of the tile loop");
   static constexpr int PV_FENCE = Bf16Cfg<D>::PV_FENCE;
   static constexpr int KS = (D + 31) / 32;  // 32-wide k-steps of the QK^T MFMA
@@ -527,18 +532,20 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
   // block by block, each block with the exponentials of one block of the
   // current tile (t -> 2^t in place).
   auto phase_a = [&](const uint16_t* ks_, Scores& sn, Scores& t) {
-    bf16x8 kf[2][KS];
-    load_kf(ks_, 0, kf[0]);
+    constexpr int KA = T::K_AHEAD;  // K blocks read ahead
+    bf16x8 kf[KA + 1][KS];
+#pragma unroll
+    for (int b = 0; b < KA && b < NB; ++b) load_kf(ks_, b, kf[b]);
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      if (b + 1 < NB) load_kf(ks_, b + 1, kf[(b + 1) & 1]);
+      if (b + KA < NB) load_kf(ks_, b + KA, kf[(b + KA) % (KA + 1)]);
       f32x4 acc[SUB];
 #pragma unroll
       for (int u = 0; u < SUB; ++u) acc[u] = zero_f32x4();
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int u = 0; u < SUB; ++u) acc[u] = mfma16x16x32_bf16(kf[b & 1][ks], qf[u][ks], acc[u]);
+        for (int u = 0; u < SUB; ++u) acc[u] = mfma16x16x32_bf16(kf[b % (KA + 1)][ks], qf[u][ks], acc[u]);
 #pragma unroll
       for (int u = 0; u < SUB; ++u)
 #pragma unroll
@@ -577,16 +584,17 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
     float mx[SUB];
 #pragma unroll
     for (int u = 0; u < SUB; ++u) mx[u] = -INFINITY;
-    bf16x8 vf[3];
-    vf[0] = load_vf(vs, 0);
-    if (J > 1) vf[1] = load_vf(vs, 1);
+    constexpr int VA = T::V_AHEAD;  // V fragments read ahead
+    bf16x8 vf[VA + 1];
+#pragma unroll
+    for (int j = 0; j < VA && j < J; ++j) vf[j] = load_vf(vs, j);
 #pragma unroll
     for (int q = 0; q < SUB; ++q) L[q] = mfma16x16x32_bf16(ones, pf[0][q], L[q]);
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      if (j + 2 < J) vf[(j + 2) % 3] = load_vf(vs, j + 2);
+      if (j + VA < J) vf[(j + VA) % (VA + 1)] = load_vf(vs, j + VA);
 #pragma unroll
-      for (int u = 0; u < SUB; ++u) O[u][j % CB] = mfma16x16x32_bf16(vf[j % 3], pf[j / CB][u], O[u][j % CB]);
+      for (int u = 0; u < SUB; ++u) O[u][j % CB] = mfma16x16x32_bf16(vf[j % (VA + 1)], pf[j / CB][u], O[u][j % CB]);
       if (j >= 1 && j - 1 < NQ - SUB) {
         const int q = SUB + j - 1;  // packed in the group before
         L[q % SUB] = mfma16x16x32_bf16(ones, pf[q / SUB][q % SUB], L[q % SUB]);
