@@ -146,7 +146,7 @@ struct Bf16Tile {
   static constexpr int KTILE = BN * D;  // elements
   static constexpr int VTILE = BN * DV;
   static constexpr int STAGE = 2 * KTILE + VTILE;
-  static_assert(NSEG % WAVES == 0, "segments split evenly over the waves");
+  static_assert(NSEG % (WAVES / 2) == 0, "segments split evenly over the loading waves");
 
   // physical 16-byte chunk of logical chunk c in K row r
   static __device__ __forceinline__ int kchunk(int r, int c) { return c ^ ((r / RPK) % NCH); }
@@ -299,13 +299,19 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
   // one 1 KB piece of the K1 (sel 0), K2 (1) or V (2) tile; which piece, its
   // LDS offset in a stage (wave-uniform), and the lane's byte offset inside
   // the tile and key row (per lane) are the same for every tile.
-  constexpr int SPW = T::NSEG / T::WAVES;  // segments per wave
+  // Only the first wave on each SIMD (waves 0..3, which the SIMD's
+  // arbitration favours and which therefore run ahead within a tile step)
+  // issues loads: the texture unit takes a tile's instructions one after the
+  // other, so an issuing wave stalls until its last one is accepted, and that
+  // stall then falls on the wave that would otherwise wait at the next barrier.
+  constexpr int LOADERS = T::WAVES / 2;
+  constexpr int SPW = T::NSEG / LOADERS;  // segments per loading wave
   int seg_sel[SPW];
   uint32_t seg_lds[SPW], seg_off[SPW];
   int seg_row[SPW];
 #pragma unroll
   for (int i = 0; i < SPW; ++i) {
-    const int seg = wave + i * T::WAVES;
+    const int seg = (wave % LOADERS) + i * LOADERS;
     if (seg < 2 * KSEG) {
       const int sg = seg % KSEG;
       const int r = sg * (64 / NCH) + lane / NCH;
@@ -332,6 +338,7 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
     const char* bk2 = (const char*)a.k2 + row0 * (2 * D);
     const char* bv = (const char*)a.v + row0 * (2 * DV);
     const uint32_t lds0 = lds_stages + (uint32_t)(buf * T::STAGE * 2);
+    if (wave >= LOADERS) return;
     if (kb + BN <= N) {
 #pragma unroll
       for (int i = 0; i < SPW; ++i)
