@@ -190,35 +190,22 @@ __device__ __forceinline__ void wait_vmem_keep() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(K) : "memory");
 }
 
+// v_max_f32 as such: the operands here are never NaN (scores, or -inf
+// where masked), so the quieting copies fmaxf would add are not needed
+__device__ __forceinline__ float max_f32(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // max over lanes l, l^16, l^32, l^48 without LDS traffic (v_permlane*_swap)
 __device__ __forceinline__ float max4_groups(float x) {
   const uint32_t xb = __builtin_bit_cast(uint32_t, x);
   auto r = __builtin_amdgcn_permlane32_swap(xb, xb, false, false);
-  x = fmaxf(u32_as_f32(r[0]), u32_as_f32(r[1]));
+  x = max_f32(u32_as_f32(r[0]), u32_as_f32(r[1]));
   const uint32_t yb = __builtin_bit_cast(uint32_t, x);
   auto q = __builtin_amdgcn_permlane16_swap(yb, yb, false, false);
-  return fmaxf(u32_as_f32(q[0]), u32_as_f32(q[1]));
-}
-
-// One map, one sub-tile: raw scores s (masked ones -inf) -> weights
-// 2^(s c - m) in place, with the threshold rescale of l and O.
-template <int NT, int CB>
-__device__ __forceinline__ void softmax_raw(float (&s)[NT], float c, float& m, f32x4& l, f32x4 (&O)[CB]) {
-  float mt = s[0];
-#pragma unroll
-  for (int i = 1; i < NT; ++i) mt = fmaxf(mt, s[i]);
-  mt = max4_groups(mt) * c;
-  if (wave_any(mt > m + kRescaleThreshold)) {
-    const float mn = fmaxf(m, mt);
-    const float alpha = (mn == -INFINITY) ? 1.0f : exp2_fast(m - mn);
-    m = mn;
-    l *= alpha;
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) O[cb] *= alpha;
-  }
-  const float nm = -m;
-#pragma unroll
-  for (int i = 0; i < NT; ++i) s[i] = exp2_fast(__builtin_fmaf(s[i], c, nm));
+  return max_f32(u32_as_f32(q[0]), u32_as_f32(q[1]));
 }
 
 template <int D, bool CAUSAL, bool NORM>
@@ -258,7 +245,7 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
     // integer division expands to vector code: keep the result scalar
     const int alt = __builtin_amdgcn_readfirstlane((G % BH == 0) ? ((G / BH - 1 - g / BH) * BH + g % BH) : (G - 1 - g));
     const int i = r * G + ((r & 1) ? alt : g);
-    return i < n_items ? i : -1;
+    return __builtin_amdgcn_readfirstlane(i < n_items ? i : -1);
   };
 
   // One item; every field is wave-uniform and kept in scalar registers.
@@ -433,26 +420,6 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
     float mt[SUB];
     const bool need = tile_max(sc, mt);
     rescale(mt, need);
-  };
-
-  // P^T = exp2(S^T c - m) rounded to bf16; chunk cc = blocks 2cc (e 0..3)
-  // and 2cc+1 (e 4..7); the row sums of the rounded P go into L
-  auto make_p = [&](const Scores& sc, PFrags& pf) {
-#pragma unroll
-    for (int cc = 0; cc < NC; ++cc)
-#pragma unroll
-      for (int u = 0; u < SUB; ++u) {
-        const float nm = -m[u];
-        u32x4 pu;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const float* sp = &sc[u][4 * (2 * cc + h)];
-          pu[2 * h] = pack_bf16x2(exp2_fast(__builtin_fmaf(sp[0], c, nm)), exp2_fast(__builtin_fmaf(sp[1], c, nm)));
-          pu[2 * h + 1] = pack_bf16x2(exp2_fast(__builtin_fmaf(sp[2], c, nm)), exp2_fast(__builtin_fmaf(sp[3], c, nm)));
-        }
-        pf[cc][u] = as_bf16x8(pu);
-        L[u] = mfma16x16x32_bf16(ones, pf[cc][u], L[u]);
-      }
   };
 
   // O^T += V^T P^T
@@ -633,7 +600,7 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
     if (wave_any(need)) {
 #pragma unroll
       for (int u = 0; u < SUB; ++u) {
-        const float dm = fmaxf(mt[u], 0.0f);
+        const float dm = max_f32(mt[u], 0.0f);
         const float alpha = exp2_fast(-dm);
         m[u] += dm;
         L[u] *= alpha;
