@@ -702,6 +702,11 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
   static_assert(CB % 2 == 0 && UR >= 1 && SUB % UR == 0 && RPB >= 1 && RG <= RPB * (STAGES - 1),
                 "epilogue exchange");
   constexpr int EPI_STORES = (SUB / UR) * (16 * UR / RPI);  // vector-memory stores per wave
+  // row pitch (elements) of the row-major staging of Y: 16 bytes more than a
+  // half row, so the 16 rows one write instruction touches fall on distinct
+  // banks, and every row stays 16-byte aligned for the 16-byte reads
+  constexpr int SP = DV / 2 + 8;
+  static_assert(16 * UR * SP * 2 <= UR * XS * 4, "staging fits the wave's send region");
   // The next item's Q rows load during the epilogue where registers allow
   // (d <= 64); otherwise after it, their latency exposed once per item.
   constexpr bool EARLY_Q = D <= 64;
@@ -771,7 +776,7 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
 #pragma unroll
           for (int j = 0; j < 4; ++j) y[j] = O[u][cb][j] * (NORM ? r * wsh[16 * cb + 4 * lg + j] : 1.0f);
           u32x2 pk = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
-          *reinterpret_cast<u32x2*>(stg + (16 * v + lr) * (DV / 2) + 16 * h + 4 * lg) = pk;
+          *reinterpret_cast<u32x2*>(stg + (16 * v + lr) * SP + 16 * h + 4 * lg) = pk;
         }
       }
       // Buffer stores against the head's N output rows: rows past N are
@@ -783,7 +788,7 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
       for (int q = 0; q < 16 * UR / RPI; ++q) {
         const int rr = q * RPI + ln / LPR;  // row within the round: 16 v + lr
         const int row = it.qw0 + 16 * (u0 + rr / 16) + rr % 16;
-        const u32x4 val = *reinterpret_cast<const u32x4*>(stg + rr * (DV / 2) + 8 * (ln % LPR));
+        const u32x4 val = *reinterpret_cast<const u32x4*>(stg + rr * SP + 8 * (ln % LPR));
         __builtin_amdgcn_raw_buffer_store_b128(val, ob, (row * DV + 16 * own0 + 8 * (ln % LPR)) * 2, 0, kStoreStreaming);
       }
       // the region is reused by the next round's sends
