@@ -11,9 +11,9 @@
 // with 12d flops per key: bound by HBM bandwidth.  Split-K: each (b, h) cache
 // is cut into S contiguous splits, one 256-thread workgroup per split.
 //   decode_split_kernel: per split, two online-softmax states (reference
-//     maximum, denominator, numerator over 2d channels); 16-byte loads, 16
-//     lanes per key row for the dots, all loads of an unrolled group issued
-//     before use; lanes that hold different keys of the same channels merge
+//     maximum, denominator, numerator over 2d channels); 16-byte
+//     non-temporal loads, 16 lanes per key row for the dots, all loads of an
+//     unrolled group issued before use; lanes that hold different keys of the same channels merge
 //     with cross-lane shuffles at the end, the 4 waves through LDS.
 //   decode_merge_kernel: per (b, h), merges the S partial states (wavefront
 //     shuffle reductions of the maxima and denominators, a fixed split order
@@ -127,12 +127,13 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     for (int u = 0; u < kUnroll; ++u) {
       const int kbase = k0 + (st0 + u * kWaves) * KPS;
       const int kr = min(kbase + kg, k1 - 1);
-      kk1[u] = ld16(K1 + (size_t)kr * D + kl * EPC);
-      kk2[u] = ld16(K2 + (size_t)kr * D + kl * EPC);
+      // the cache is read once: non-temporal loads keep it from churning the caches
+      kk1[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(K1 + (size_t)kr * D + kl * EPC));
+      kk2[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(K2 + (size_t)kr * D + kl * EPC));
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
         const int vr = min(kbase + x * VKPL + vg, k1 - 1);
-        vv[u][x] = ld16(V + (size_t)vr * DV + vl * EPC);
+        vv[u][x] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(V + (size_t)vr * DV + vl * EPC));
       }
     }
 #pragma unroll
