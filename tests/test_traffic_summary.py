@@ -38,3 +38,19 @@ def test_traffic_scaled_by_the_calibration_copy(tmp_path):
     assert t["write_bytes"] == 50 * 1024
     assert t["bytes_per_launch"] == t["fetch_bytes"] + t["write_bytes"]
     assert len(t["source_sha256_16"]) == 16
+
+
+def test_traffic_of_a_two_kernel_step(tmp_path):
+    fetch, write = tmp_path / "f.csv", tmp_path / "w.csv"
+    _write(fetch, [("split_kernel<x>", "FETCH_SIZE", 1000.0), ("merge_kernel<x>", "FETCH_SIZE", 10.0),
+                   ("__amd_rocclr_copyBuffer", "FETCH_SIZE", 1024.0)])
+    _write(write, [("split_kernel<x>", "WRITE_SIZE", 100.0), ("merge_kernel<x>", "WRITE_SIZE", 1.0),
+                   ("__amd_rocclr_copyBuffer", "WRITE_SIZE", 1024.0)])
+    out = subprocess.run(
+        [sys.executable, "-m", "transformer_attention_diffattn_amd.traffic_summary", "--fetch", str(fetch),
+         "--write", str(write), "--kernel", "split_kernel", "--kernel", "merge_kernel", "--name", "x",
+         "--workload", "y", "--source", "decode.hip", "--calib-mib", "1", "--algorithmic", "1"],
+        capture_output=True, text=True, check=True, cwd=ROOT).stdout
+    t = json.loads(out)
+    assert t["fetch_bytes"] == 1010 * 1024 and t["write_bytes"] == 101 * 1024
+    assert t["kernel"] == "split_kernel + merge_kernel"

@@ -7,6 +7,10 @@
         --workload layer1p4b_bf16_b4h16n2048d64 --source prefill.hip \\
         --calib-mib 1024 --algorithmic 134217728 > profiles/prefill_layer1p4b_traffic.json
 
+``--kernel`` may be given more than once (a step of several kernels, such as
+decode's split and merge kernels): the figure is then the sum of each
+kernel's per-dispatch mean.
+
 The passes are runs of ``bench.py ... --copy-calib-mib M``, which also makes
 one device copy of M MiB.  FETCH_SIZE and WRITE_SIZE are in KiB per dispatch;
 each is scaled by the factor that makes the copy read and write exactly M MiB
@@ -51,30 +55,35 @@ def main() -> None:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--fetch", required=True)
     ap.add_argument("--write", required=True)
-    ap.add_argument("--kernel", required=True, help="substring of the kernel name")
+    ap.add_argument("--kernel", required=True, action="append", help="substring of a kernel name (repeatable)")
     ap.add_argument("--name", required=True)
     ap.add_argument("--workload", required=True)
     ap.add_argument("--source", required=True, help="csrc file(s) the kernel is built from, comma separated")
     ap.add_argument("--calib-mib", type=int, required=True)
     ap.add_argument("--algorithmic", type=int, required=True, help="algorithmic bytes per launch")
     a = ap.parse_args()
-    f = _per_dispatch(a.fetch, a.kernel)
-    w = _per_dispatch(a.write, a.kernel)
-    if not f or not w:
-        raise SystemExit(f"no dispatch of {a.kernel!r} in the counter files")
+    fetch_kib = write_kib = 0.0
+    counts = []
+    for k in a.kernel:
+        f = _per_dispatch(a.fetch, k)
+        w = _per_dispatch(a.write, k)
+        if not f or not w:
+            raise SystemExit(f"no dispatch of {k!r} in the counter files")
+        fetch_kib += sum(f) / len(f)
+        write_kib += sum(w) / len(w)
+        counts.append(len(f))
     calib_kib = a.calib_mib * 1024.0
     cf, cw = _copy_value(a.fetch), _copy_value(a.write)
     if cf <= 0 or cw <= 0:
         raise SystemExit("no calibration copy found in the counter files")
     ff, fw = calib_kib / cf, calib_kib / cw
-    fetch_kib, write_kib = sum(f) / len(f), sum(w) / len(w)
     h = hashlib.sha256()
     for n in a.source.split(","):
         with open(os.path.join(PKG, "csrc", n), "rb") as fh:
             h.update(fh.read())
     fetch_b, write_b = fetch_kib * ff * 1024, write_kib * fw * 1024
     out = {
-        "kernel": a.kernel, "workload": a.workload, "dispatches": len(f),
+        "kernel": " + ".join(a.kernel), "workload": a.workload, "dispatches": min(counts),
         "fetch_kib_raw": fetch_kib, "write_kib_raw": write_kib,
         "fetch_factor": ff, "write_factor": fw,
         "bytes_per_launch": int(round(fetch_b + write_b)),
