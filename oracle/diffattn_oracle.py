@@ -33,6 +33,12 @@ the design notes of the repository):
 * decode attends the first cache_len[b] cached keys; a sequence with
   cache_len 0 attends nothing and its output is defined as zero.
 
+The gradients (``backward``) are those of the same definitions: training is
+the pages' workload (page 3, "Summary": lambda is learnable through its
+vectors, and the normalised outputs are trained end to end), and the
+derivative of a composition of softmax, a matrix product and RMSNorm is fixed
+by the forward.  lambda_init is a schedule constant and gets no gradient.
+
 Every function below is pinned by ``tests/test_oracle.py`` against facts that
 do not come from this file: the printed example values, closed forms,
 invariants, and library routines (torch's scaled_dot_product_attention and
@@ -55,6 +61,8 @@ __all__ = [
     "forward",
     "forward_rows",
     "decode",
+    "map_stats",
+    "backward",
 ]
 
 
@@ -204,3 +212,81 @@ def decode(q1, q2, k1c, k2c, vc, cache_len, lam: float, lambda_init: float,
                          _f64(vc[b, h, :n]), lam, causal=False)
             out[b, h] = (head_rmsnorm_scale(y, weight, eps, lambda_init) if norm else y)[0]
     return out
+
+
+def map_stats(q1, k1, q2, k2, v, causal: bool = True):
+    """Per-map row statistics of the forward, for one head.
+
+    q1, k1, q2, k2: [N, d]; v: [N, 2d].  Returns (lse1, lse2, o1, o2):
+    lse_k[i] = log sum_j exp(s_k[i, j]) over visible keys (natural log, with
+    s_k = Q_k K_k^T / sqrt d) and o_k = softmax(s_k) V, the per-map outputs
+    whose difference o1 - lambda o2 is Y (Eq. 1, by linearity).
+    """
+    q1, k1, q2, k2, v = (_f64(t) for t in (q1, k1, q2, k2, v))
+    d = q1.shape[-1]
+    vis = _visible(q1.shape[0], k1.shape[0], causal)
+    res = []
+    for q, k in ((q1, k1), (q2, k2)):
+        s = np.where(vis, (q @ k.T) / math.sqrt(d), -np.inf)
+        m = np.max(s, axis=-1, keepdims=True)
+        lse = (m + np.log(np.sum(np.exp(s - m), axis=-1, keepdims=True)))[:, 0]
+        res.append((lse, softmax_rows(s) @ v))
+    return res[0][0], res[1][0], res[0][1], res[1][1]
+
+
+def backward(q1, k1, q2, k2, v, lq1, lk1, lq2, lk2, lambda_init: float, dout,
+             weight=None, eps: float = 1e-5, causal: bool = True) -> dict:
+    """Gradients of L = sum(out * dout) for the forward of ``forward``.
+
+    q1, k1, q2, k2: [B, H, N, d]; v, dout: [B, H, N, 2d]; lambda vectors [d];
+    weight [2d] or None (ones).  Chain rule through the definitions, step by
+    step (sigma = 1 - lambda_init, n = 2d, per row i):
+
+    * Eq. 3: out = sigma w Y / r with r = sqrt(mean(Y^2) + eps), so
+      dw = sum over rows of sigma dout Y / r, and with g = sigma w dout,
+      dY = g / r - Y (g . Y) / (n r^3);
+    * Eq. 1: Y = A1 V - lambda A2 V, so dV = (A1 - lambda A2)^T dY,
+      dA1 = dY V^T, dA2 = -lambda dY V^T, dlambda = -sum(A2 * dY V^T);
+    * softmax: dS = A * (dA - rowsum(A * dA)), then with S = Q K^T / sqrt d,
+      dQ = dS K / sqrt d and dK = dS^T Q / sqrt d;
+    * Eq. 2: lambda = exp(lq1.lk1) - exp(lq2.lk2) + lambda_init, so
+      dlq1 = dlambda exp(lq1.lk1) lk1, dlk1 = dlambda exp(lq1.lk1) lq1 and
+      the map-2 pair with the opposite sign.
+
+    Returns float64 arrays dq1, dk1, dq2, dk2, dv, dweight, dlq1, dlk1, dlq2,
+    dlk2 and the scalar dlambda.
+    """
+    q1, k1, q2, k2, v, g_out = (_f64(t) for t in (q1, k1, q2, k2, v, dout))
+    lq1, lk1, lq2, lk2 = (_f64(t) for t in (lq1, lk1, lq2, lk2))
+    lam = lambda_scalar(lq1, lk1, lq2, lk2, lambda_init)
+    sigma = 1.0 - float(lambda_init)
+    B, H, N, d = q1.shape
+    n = v.shape[-1]
+    w = np.ones(n) if weight is None else _f64(weight)
+    vis = _visible(N, N, causal)
+    grads = {k: np.zeros_like(t) for k, t in (("dq1", q1), ("dk1", k1), ("dq2", q2), ("dk2", k2), ("dv", v))}
+    dweight = np.zeros(n)
+    dlam = 0.0
+    for b in range(B):
+        for h in range(H):
+            a1 = softmax_rows(np.where(vis, (q1[b, h] @ k1[b, h].T) / math.sqrt(d), -np.inf))
+            a2 = softmax_rows(np.where(vis, (q2[b, h] @ k2[b, h].T) / math.sqrt(d), -np.inf))
+            y = (a1 - lam * a2) @ v[b, h]
+            r = np.sqrt(np.mean(y * y, axis=-1, keepdims=True) + float(eps))
+            go = g_out[b, h]
+            dweight += np.sum(sigma * go * y / r, axis=0)
+            g = sigma * w * go
+            dy = g / r - y * np.sum(g * y, axis=-1, keepdims=True) / (n * r ** 3)
+            grads["dv"][b, h] = (a1 - lam * a2).T @ dy
+            da = dy @ v[b, h].T  # dL/dA1; dL/dA2 = -lam * da
+            dlam += -float(np.sum(a2 * da))
+            for a, dak, q, k, dq, dk in ((a1, da, q1, k1, "dq1", "dk1"), (a2, -lam * da, q2, k2, "dq2", "dk2")):
+                ds = a * (dak - np.sum(a * dak, axis=-1, keepdims=True))
+                grads[dq][b, h] = ds @ k[b, h] / math.sqrt(d)
+                grads[dk][b, h] = ds.T @ q[b, h] / math.sqrt(d)
+    e1 = math.exp(float(np.dot(lq1, lk1)))
+    e2 = math.exp(float(np.dot(lq2, lk2)))
+    grads.update(dweight=dweight, dlambda=dlam,
+                 dlq1=dlam * e1 * lk1, dlk1=dlam * e1 * lq1,
+                 dlq2=-dlam * e2 * lk2, dlk2=-dlam * e2 * lq2)
+    return grads
