@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define DIFFATTN_ABI_VERSION 1
+#define DIFFATTN_ABI_VERSION 2
 
 #if defined(__GNUC__) || defined(__clang__)
 #define DIFFATTN_API __attribute__((visibility("default")))
@@ -58,7 +58,7 @@ typedef enum {
   DIFFATTN_EINVAL = 1,       /* null/misaligned pointer, negative size, bad flag  */
   DIFFATTN_EUNSUPPORTED = 2, /* d or dtype outside the supported set              */
   DIFFATTN_EHIP = 3,         /* a HIP launch or query failed                      */
-  DIFFATTN_EWORKSPACE = 4    /* decode workspace missing or too small             */
+  DIFFATTN_EWORKSPACE = 4    /* workspace missing or too small                    */
 } diffattn_status;
 
 typedef enum { DIFFATTN_FP32 = 0, DIFFATTN_BF16 = 1 } diffattn_dtype;
@@ -129,6 +129,74 @@ DIFFATTN_API diffattn_status diffattn_decode(diffattn_dtype dt, const void* q1, 
                                 const int* cache_len, void* out, int B, int H, int L_max, int d,
                                 const float* lambda, float lambda_init, const float* norm_weight,
                                 float eps, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Training: the gradients of the same forward.  The review page's "Summary"
+ * describes the layer as trained end to end (lambda through its vectors,
+ * Eq. 2; the per-head normalisation of Eq. 3); the derivatives follow from
+ * Eq. 1-3 by the chain rule.  lambda_init is a schedule constant and gets no
+ * gradient.  Supported: dt = BF16 and d in {32, 64, 128}; other values return
+ * DIFFATTN_EUNSUPPORTED.
+ *
+ * diffattn_fwd_train -- diffattn_fwd (same arguments, NO_NORM not allowed)
+ * that also keeps what the backward needs:
+ *   lse : device fp32 [2, B, H, N]: per map k and row i, the log2-sum-exp
+ *         log2(sum_j 2^(s_k[i,j] log2(e))) of the scaled scores
+ *         s_k = Q_k K_k^T / sqrt(d) over the visible keys;
+ *   o12 : device fp32 [2, B, H, N, 2d]: per map, softmax(s_k) V (so that
+ *         Y = o12[0] - lambda o12[1]).
+ * Both 16-byte aligned and written in full for rows < N.
+ */
+DIFFATTN_API diffattn_status diffattn_fwd_train(diffattn_dtype dt, const void* q1, const void* k1,
+                                   const void* q2, const void* k2, const void* v, void* out, int B,
+                                   int H, int N, int d, const float* lambda, float lambda_init,
+                                   const float* norm_weight, float eps, unsigned flags, float* lse,
+                                   float* o12, void* stream);
+
+/*
+ * diffattn_bwd_workspace_bytes -- device scratch bytes that diffattn_bwd
+ * needs for these sizes (0 if they are invalid, empty or unsupported).
+ */
+DIFFATTN_API size_t diffattn_bwd_workspace_bytes(int B, int H, int N, int d);
+
+/*
+ * diffattn_bwd -- gradients of L = sum(out * dout) for one diffattn_fwd_train
+ * call with the same inputs, lambda, lambda_init, norm_weight, eps and flags.
+ *   q1..v, lambda, lambda_init, norm_weight, eps, flags : as for the forward
+ *                    (flags: DIFFATTN_CAUSAL or 0)
+ *   dout           : [B, H, N, 2d] of dtype dt
+ *   lse, o12       : the training forward's outputs (read only)
+ *   dq1, dk1, dq2, dk2 : [B, H, N, d] of dtype dt, written in full
+ *   dv             : [B, H, N, 2d] of dtype dt, written in full
+ *   dlambda        : device fp32 [1]: dL/dlambda (summed over all rows);
+ *                    diffattn_lambda_bwd takes it to the lambda vectors
+ *   dweight        : device fp32 [2d]: dL/dnorm_weight (written even when
+ *                    norm_weight is NULL, as the gradient at ones)
+ *   workspace      : at least diffattn_bwd_workspace_bytes(B, H, N, d) bytes,
+ *                    256-byte aligned, no initialisation needed; calls that
+ *                    share it must be ordered on one stream.
+ * Products are bf16 matrix operations with fp32 accumulation; the softmax
+ * weights and the gradient of Y enter them rounded to bf16.  dQ is computed
+ * apart from dK/dV (no atomics), and the sums over rows (dweight, dlambda)
+ * are added in a fixed order, so results are deterministic.  Outputs must
+ * not alias inputs.
+ */
+DIFFATTN_API diffattn_status diffattn_bwd(diffattn_dtype dt, const void* q1, const void* k1, const void* q2,
+                             const void* k2, const void* v, const void* dout, const float* lse,
+                             const float* o12, int B, int H, int N, int d, const float* lambda,
+                             float lambda_init, const float* norm_weight, float eps, unsigned flags,
+                             void* dq1, void* dk1, void* dq2, void* dk2, void* dv, float* dlambda,
+                             float* dweight, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * diffattn_lambda_bwd -- Eq. 2 backward: with e1 = exp(lq1 . lk1) and
+ * e2 = exp(lq2 . lk2), dlq1 = g e1 lk1, dlk1 = g e1 lq1, dlq2 = -g e2 lk2,
+ * dlk2 = -g e2 lq2, where g = dlambda[0] (device fp32, e.g. from
+ * diffattn_bwd).  All vectors are device fp32 [d], d in 1..4096.
+ */
+DIFFATTN_API diffattn_status diffattn_lambda_bwd(const float* lq1, const float* lk1, const float* lq2,
+                                    const float* lk2, int d, const float* dlambda, float* dlq1,
+                                    float* dlk1, float* dlq2, float* dlk2, void* stream);
 
 /* Static English text for a status code (never NULL). */
 DIFFATTN_API const char* diffattn_strerror(diffattn_status status);

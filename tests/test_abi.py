@@ -35,8 +35,9 @@ def L():
 
 def test_header_declares_the_abi():
     assert declared_symbols() == sorted([
-        "diffattn_abi_version", "diffattn_decode", "diffattn_decode_workspace_bytes",
-        "diffattn_fwd", "diffattn_lambda", "diffattn_strerror"])
+        "diffattn_abi_version", "diffattn_bwd", "diffattn_bwd_workspace_bytes", "diffattn_decode",
+        "diffattn_decode_workspace_bytes", "diffattn_fwd", "diffattn_fwd_train", "diffattn_lambda",
+        "diffattn_lambda_bwd", "diffattn_strerror"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -50,7 +51,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_strerror(L):
-    assert L.diffattn_abi_version() == 1
+    assert L.diffattn_abi_version() == 2
     for code in range(5):
         assert L.diffattn_strerror(code)
     assert L.diffattn_strerror(99) == b"unknown status"

@@ -44,6 +44,15 @@ def lib() -> ctypes.CDLL:
         L.diffattn_decode.restype = i
         L.diffattn_strerror.argtypes = [i]
         L.diffattn_strerror.restype = ctypes.c_char_p
+        L.diffattn_fwd_train.argtypes = [i, vp, vp, vp, vp, vp, vp, i, i, i, i, vp, f, vp, f, u, vp, vp, vp]
+        L.diffattn_fwd_train.restype = i
+        L.diffattn_bwd_workspace_bytes.argtypes = [i, i, i, i]
+        L.diffattn_bwd_workspace_bytes.restype = sz
+        L.diffattn_bwd.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, vp, f, vp, f, u,
+                                   vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.diffattn_bwd.restype = i
+        L.diffattn_lambda_bwd.argtypes = [vp, vp, vp, vp, i, vp, vp, vp, vp, vp, vp]
+        L.diffattn_lambda_bwd.restype = i
         L.diffattn_abi_version.argtypes = []
         L.diffattn_abi_version.restype = i
         _lib = L
@@ -157,3 +166,79 @@ def decode(q1, q2, k1c, k2c, vc, lam_t, lambda_init: float, cache_len=None, weig
                                  _ptr(weight), float(eps), _ptr(workspace), workspace.numel(),
                                  _stream(q1.device)), "diffattn_decode")
     return out
+
+
+def _check_qkv(q1, k1, q2, k2, v):
+    for n, t in (("q1", q1), ("k1", k1), ("q2", q2), ("k2", k2), ("v", v)):
+        _dev(t, n)
+    if q1.dtype != torch.bfloat16:
+        raise ValueError("training entry points take bfloat16 tensors")
+    B, H, N, d = q1.shape
+    for n, t in (("k1", k1), ("q2", q2), ("k2", k2)):
+        if t.shape != q1.shape or t.dtype != q1.dtype:
+            raise ValueError(f"{n} must match q1 in shape and dtype")
+    if v.shape != (B, H, N, 2 * d) or v.dtype != q1.dtype:
+        raise ValueError("v must be [B,H,N,2d] of q1's dtype")
+    return B, H, N, d
+
+
+def fwd_train(q1, k1, q2, k2, v, lam_t, lambda_init: float, weight=None, eps: float = 1e-5,
+              causal: bool = True):
+    """Training forward: returns (out [B,H,N,2d] bf16, lse [2,B,H,N] fp32 in
+    log2 units, o12 [2,B,H,N,2d] fp32 per-map outputs)."""
+    B, H, N, d = _check_qkv(q1, k1, q2, k2, v)
+    _dev(lam_t, "lambda")
+    if weight is not None:
+        _dev(weight, "weight")
+    out = torch.empty_like(v)
+    lse = torch.empty((2, B, H, N), dtype=torch.float32, device=q1.device)
+    o12 = torch.empty((2, B, H, N, 2 * d), dtype=torch.float32, device=q1.device)
+    _check(lib().diffattn_fwd_train(BF16, _ptr(q1), _ptr(k1), _ptr(q2), _ptr(k2), _ptr(v), _ptr(out),
+                                    B, H, N, d, _ptr(lam_t), float(lambda_init), _ptr(weight), float(eps),
+                                    CAUSAL if causal else 0, _ptr(lse), _ptr(o12), _stream(q1.device)),
+           "diffattn_fwd_train")
+    return out, lse, o12
+
+
+def bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
+    return int(lib().diffattn_bwd_workspace_bytes(B, H, N, d))
+
+
+def bwd(q1, k1, q2, k2, v, dout, lse, o12, lam_t, lambda_init: float, weight=None, eps: float = 1e-5,
+        causal: bool = True, workspace=None, grads=None):
+    """Backward of ``fwd_train``: returns a dict with dq1, dk1, dq2, dk2, dv
+    (bf16) and dlambda [1], dweight [2d] (fp32)."""
+    B, H, N, d = _check_qkv(q1, k1, q2, k2, v)
+    for n, t in (("dout", dout), ("lse", lse), ("o12", o12), ("lambda", lam_t)):
+        _dev(t, n)
+    if dout.shape != v.shape or dout.dtype != v.dtype:
+        raise ValueError("dout must match v")
+    if lse.shape != (2, B, H, N) or o12.shape != (2, B, H, N, 2 * d):
+        raise ValueError("lse / o12 must come from fwd_train on the same shapes")
+    if weight is not None:
+        _dev(weight, "weight")
+    dev = q1.device
+    if grads is None:
+        grads = dict(dq1=torch.empty_like(q1), dk1=torch.empty_like(k1), dq2=torch.empty_like(q2),
+                     dk2=torch.empty_like(k2), dv=torch.empty_like(v),
+                     dlambda=torch.empty(1, dtype=torch.float32, device=dev),
+                     dweight=torch.empty(2 * d, dtype=torch.float32, device=dev))
+    if workspace is None:
+        workspace = torch.empty(max(bwd_workspace_bytes(B, H, N, d), 256), dtype=torch.uint8, device=dev)
+    g = grads
+    _check(lib().diffattn_bwd(BF16, _ptr(q1), _ptr(k1), _ptr(q2), _ptr(k2), _ptr(v), _ptr(dout), _ptr(lse),
+                              _ptr(o12), B, H, N, d, _ptr(lam_t), float(lambda_init), _ptr(weight), float(eps),
+                              CAUSAL if causal else 0, _ptr(g["dq1"]), _ptr(g["dk1"]), _ptr(g["dq2"]),
+                              _ptr(g["dk2"]), _ptr(g["dv"]), _ptr(g["dlambda"]), _ptr(g["dweight"]),
+                              _ptr(workspace), workspace.numel(), _stream(dev)), "diffattn_bwd")
+    return grads
+
+
+def lambda_bwd(lq1, lk1, lq2, lk2, dlambda):
+    """Eq. 2 backward: (dlq1, dlk1, dlq2, dlk2), fp32 [d] each."""
+    for n, t in (("lq1", lq1), ("lk1", lk1), ("lq2", lq2), ("lk2", lk2), ("dlambda", dlambda)):
+        _dev(t, n)
+    outs = [torch.empty_like(lq1) for _ in range(4)]
+    _check(lib().diffattn_lambda_bwd(_ptr(lq1), _ptr(lk1), _ptr(lq2), _ptr(lk2), lq1.numel(), _ptr(dlambda),
+                                     *[_ptr(o) for o in outs], _stream(lq1.device)), "diffattn_lambda_bwd")
+    return tuple(outs)

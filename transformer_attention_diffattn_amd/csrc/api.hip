@@ -44,6 +44,7 @@ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 bool ok_ptr16(const void* p) { return p != nullptr && aligned(p, 16); }
 bool ok_ptr4(const void* p) { return p != nullptr && aligned(p, 4); }
 bool supported_d(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool supported_bwd_d(int d) { return d == 32 || d == 64 || d == 128; }
 bool finite_nonneg(float x) { return isfinite(x) && x >= 0.f; }
 
 }  // namespace
@@ -58,7 +59,7 @@ const char* diffattn_strerror(diffattn_status s) {
     case DIFFATTN_EINVAL: return "invalid argument (null or misaligned pointer, negative size, bad flag or eps)";
     case DIFFATTN_EUNSUPPORTED: return "unsupported dtype or head width d (d must be 16, 32, 64 or 128)";
     case DIFFATTN_EHIP: return "HIP launch or runtime error";
-    case DIFFATTN_EWORKSPACE: return "decode workspace missing or smaller than diffattn_decode_workspace_bytes()";
+    case DIFFATTN_EWORKSPACE: return "workspace missing or smaller than the size its *_workspace_bytes() call gives";
     default: return "unknown status";
   }
 }
@@ -72,10 +73,10 @@ diffattn_status diffattn_lambda(const float* lq1, const float* lk1, const float*
   return e == hipSuccess ? DIFFATTN_OK : DIFFATTN_EHIP;
 }
 
-diffattn_status diffattn_fwd(diffattn_dtype dt, const void* q1, const void* k1, const void* q2, const void* k2,
-                             const void* v, void* out, int B, int H, int N, int d, const float* lambda,
-                             float lambda_init, const float* norm_weight, float eps, unsigned flags,
-                             void* stream) {
+static diffattn_status fwd_impl(diffattn_dtype dt, const void* q1, const void* k1, const void* q2, const void* k2,
+                                const void* v, void* out, int B, int H, int N, int d, const float* lambda,
+                                float lambda_init, const float* norm_weight, float eps, unsigned flags,
+                                float* lse, float* osave, void* stream) {
   if (dt != DIFFATTN_FP32 && dt != DIFFATTN_BF16) return DIFFATTN_EUNSUPPORTED;
   if (!supported_d(d)) return DIFFATTN_EUNSUPPORTED;
   if (B < 0 || H < 0 || N < 0) return DIFFATTN_EINVAL;
@@ -110,7 +111,115 @@ diffattn_status diffattn_fwd(diffattn_dtype dt, const void* q1, const void* k1, 
   a.norm_w = norm_weight;
   a.eps = eps;
   a.c = (float)(1.4426950408889634 / sqrt((double)d));
+  a.lse = lse;
+  a.osave = osave;
   hipError_t e = diffattn::launch_prefill(bf16, d, (flags & DIFFATTN_CAUSAL) != 0, norm, a, (hipStream_t)stream);
+  return e == hipSuccess ? DIFFATTN_OK : DIFFATTN_EHIP;
+}
+
+diffattn_status diffattn_fwd(diffattn_dtype dt, const void* q1, const void* k1, const void* q2, const void* k2,
+                             const void* v, void* out, int B, int H, int N, int d, const float* lambda,
+                             float lambda_init, const float* norm_weight, float eps, unsigned flags,
+                             void* stream) {
+  return fwd_impl(dt, q1, k1, q2, k2, v, out, B, H, N, d, lambda, lambda_init, norm_weight, eps, flags, nullptr,
+                  nullptr, stream);
+}
+
+diffattn_status diffattn_fwd_train(diffattn_dtype dt, const void* q1, const void* k1, const void* q2,
+                                   const void* k2, const void* v, void* out, int B, int H, int N, int d,
+                                   const float* lambda, float lambda_init, const float* norm_weight, float eps,
+                                   unsigned flags, float* lse, float* o12, void* stream) {
+  if (dt != DIFFATTN_BF16 || !supported_bwd_d(d)) return DIFFATTN_EUNSUPPORTED;
+  if (flags & DIFFATTN_NO_NORM) return DIFFATTN_EINVAL;
+  if (B < 0 || H < 0 || N < 0) return DIFFATTN_EINVAL;
+  if ((long long)B * H * N == 0) return DIFFATTN_OK;
+  if (!ok_ptr16(lse) || !ok_ptr16(o12)) return DIFFATTN_EINVAL;
+  return fwd_impl(dt, q1, k1, q2, k2, v, out, B, H, N, d, lambda, lambda_init, norm_weight, eps, flags, lse, o12,
+                  stream);
+}
+
+// workspace layout of diffattn_bwd: dY (bf16), delta (fp32), partial sums
+static size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+static void bwd_layout(int B, int H, int N, int d, size_t* off_delta, size_t* off_part, size_t* total) {
+  const size_t rows = (size_t)B * H * N;
+  const size_t dy = round256(rows * 2 * d * 2);
+  const size_t delta = round256(rows * 2 * 4);
+  const size_t part = round256((size_t)diffattn::bwd_prep_blocks((long long)rows) * (2 * d + 1) * 4);
+  *off_delta = dy;
+  *off_part = dy + delta;
+  *total = dy + delta + part;
+}
+
+size_t diffattn_bwd_workspace_bytes(int B, int H, int N, int d) {
+  if (B <= 0 || H <= 0 || N <= 0 || !supported_bwd_d(d)) return 0;
+  size_t od, op, total;
+  bwd_layout(B, H, N, d, &od, &op, &total);
+  return total;
+}
+
+diffattn_status diffattn_bwd(diffattn_dtype dt, const void* q1, const void* k1, const void* q2, const void* k2,
+                             const void* v, const void* dout, const float* lse, const float* o12, int B, int H,
+                             int N, int d, const float* lambda, float lambda_init, const float* norm_weight,
+                             float eps, unsigned flags, void* dq1, void* dk1, void* dq2, void* dk2, void* dv,
+                             float* dlambda, float* dweight, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  if (dt != DIFFATTN_BF16 || !supported_bwd_d(d)) return DIFFATTN_EUNSUPPORTED;
+  if (B < 0 || H < 0 || N < 0) return DIFFATTN_EINVAL;
+  if (flags & ~DIFFATTN_CAUSAL) return DIFFATTN_EINVAL;
+  if (!finite_nonneg(eps) || !isfinite(lambda_init)) return DIFFATTN_EINVAL;
+  if ((long long)B * H * N == 0) return DIFFATTN_OK;  // empty work: pointers are not inspected
+  const void* in16[] = {q1, k1, q2, k2, v, dout, lse, o12, dq1, dk1, dq2, dk2, dv};
+  for (const void* p : in16)
+    if (!ok_ptr16(p)) return DIFFATTN_EINVAL;
+  if (!ok_ptr4(lambda) || !ok_ptr4(dlambda) || !ok_ptr4(dweight)) return DIFFATTN_EINVAL;
+  if (norm_weight && !aligned(norm_weight, 4)) return DIFFATTN_EINVAL;
+  const long long BH = (long long)B * H;
+  // grids of (N / 64) x BH workgroups and row indices below 2^31 per head
+  if (BH > INT32_MAX || ((long long)N + 63) / 64 * BH > (long long)INT32_MAX) return DIFFATTN_EINVAL;
+  size_t od, op, total;
+  bwd_layout(B, H, N, d, &od, &op, &total);
+  if (workspace == nullptr || workspace_bytes < total) return DIFFATTN_EWORKSPACE;
+  if (!aligned(workspace, 256)) return DIFFATTN_EINVAL;
+
+  diffattn::BwdArgs a;
+  a.q1 = q1;
+  a.k1 = k1;
+  a.q2 = q2;
+  a.k2 = k2;
+  a.v = v;
+  a.dout = dout;
+  a.lse = lse;
+  a.osave = o12;
+  a.dq1 = dq1;
+  a.dk1 = dk1;
+  a.dq2 = dq2;
+  a.dk2 = dk2;
+  a.dv = dv;
+  a.dweight = dweight;
+  a.dlambda = dlambda;
+  a.dy = (uint16_t*)workspace;
+  a.delta = (float*)((char*)workspace + od);
+  a.partial = (float*)((char*)workspace + op);
+  a.BH = (int)BH;
+  a.N = N;
+  a.lambda = lambda;
+  a.out_scale = 1.0f - lambda_init;
+  a.norm_w = norm_weight;
+  a.eps = eps;
+  a.c = (float)(1.4426950408889634 / sqrt((double)d));
+  hipError_t e = diffattn::launch_bwd(d, (flags & DIFFATTN_CAUSAL) != 0, a, (hipStream_t)stream);
+  return e == hipSuccess ? DIFFATTN_OK : DIFFATTN_EHIP;
+}
+
+diffattn_status diffattn_lambda_bwd(const float* lq1, const float* lk1, const float* lq2, const float* lk2, int d,
+                                    const float* dlambda, float* dlq1, float* dlk1, float* dlq2, float* dlk2,
+                                    void* stream) {
+  const float* in4[] = {lq1, lk1, lq2, lk2, dlambda, dlq1, dlk1, dlq2, dlk2};
+  for (const float* p : in4)
+    if (!ok_ptr4(p)) return DIFFATTN_EINVAL;
+  if (d < 1 || d > 4096) return DIFFATTN_EINVAL;
+  hipError_t e = diffattn::launch_lambda_bwd(lq1, lk1, lq2, lk2, d, dlambda, dlq1, dlk1, dlq2, dlk2,
+                                             (hipStream_t)stream);
   return e == hipSuccess ? DIFFATTN_OK : DIFFATTN_EHIP;
 }
 

@@ -1,0 +1,486 @@
+// Backward of the fused differential-attention forward for gfx950 (MI355X).
+//
+// The gradients follow from the forward's definitions (Eq. 1 of "Differential
+// Transformer: Canceling Context Noise with Differential Attention", section
+// "Cancelling Context Noise Through Attention Map Subtraction"; Eq. 2 and
+// Eq. 3 of the "Differential Transformer" sample review, "Summary", with the
+// head-wise RMSNorm of its "Weaknesses"), which the review's "Summary"
+// describes as trained end to end.  Per row i (sigma = 1 - lambda_init,
+// n = 2d, r = sqrt(mean(Y^2) + eps), g = sigma w dout):
+//
+//   dY    = g / r - Y (g . Y) / (n r^3)            dw = sum_i sigma dout Y / r
+//   dV    = (A1 - lambda A2)^T dY                  dP = dY V^T
+//   dS1   = A1 * (dP - delta1),  delta1 = dY . O1  (O_k = A_k V)
+//   dS2   = A2 * (-lambda dP - delta2),  delta2 = -lambda dY . O2
+//   dQk   = dSk Kk / sqrt d,  dKk = dSk^T Qk / sqrt d
+//   dlambda = -sum_i dY . O2
+//
+// The forward run in training mode keeps, per map and row, the log2-sum-exp
+// of the scaled scores and O_k; A_k is recomputed here as
+// 2^(s log2(e)/sqrt(d) - lse_k).  Four launches:
+//   bwd_prep_kernel    row-wise: Y, r, dY (bf16), delta1, delta2, and per-
+//                      workgroup partial sums of dw and dlambda;
+//   bwd_dq_kernel      query-parallel: S^T, dP^T and dQ^T += K^T dS^T;
+//   bwd_dkv_kernel     key-parallel: S, dP and dV^T += dY^T D,
+//                      dK^T += Q^T dS (D = A1 - lambda A2);
+//   bwd_reduce_kernel  the partial sums in a fixed order (deterministic).
+// Splitting dQ from dK/dV costs a second evaluation of S and dP but needs no
+// atomics, so every gradient is deterministic.
+//
+// All products use the 16x16x32 bf16 MFMA with fp32 accumulation.  Staged
+// tiles live in LDS as [16-column block][row][16 columns]: a 16-byte read
+// gives an A operand whose k runs over columns, and the transposing read
+// (lds_read_tr16) one whose k runs over rows.  A 16x16 result C holds, in
+// lane L, column L % 16 and rows 4 (L / 16) + j; two such blocks over 32 rows,
+// rounded to bf16 in-lane, are the B operand of a product whose k runs over
+// those rows, in the same row order as the transposing read delivers them.
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace diffattn {
+
+namespace {
+
+// element offset of (row r, column c) in an R-row tile stored as
+// [16-column block][row][16 columns]
+template <int R>
+__device__ __forceinline__ int boff(int r, int c) {
+  return ((c >> 4) * R + r) * 16 + (c & 15);
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+// Copy rows [r0, r0 + R) of a row-major [*, C] bf16 matrix (rows past
+// n_rows - 1 read row n_rows - 1) into an R x C blocked LDS tile.
+template <int R, int C, int NT>
+__device__ __forceinline__ void stage_tile(uint16_t* __restrict__ dst, const uint16_t* __restrict__ src, int r0,
+                                           int n_rows, int tid) {
+  constexpr int CH = R * C / 8;  // 16-byte chunks
+#pragma unroll
+  for (int i = 0; i < (CH + NT - 1) / NT; ++i) {
+    const int idx = tid + i * NT;
+    if (CH % NT == 0 || idx < CH) {
+      const int r = idx / (C / 8), c8 = idx % (C / 8);
+      const int gr = min(r0 + r, n_rows - 1);
+      st16(dst + boff<R>(r, 8 * c8), ld16(src + (size_t)gr * C + 8 * c8));
+    }
+  }
+}
+
+// A operand with k over 32 rows starting at r0 of column block cb (R-row tile)
+template <int R>
+__device__ __forceinline__ bf16x8 tr_frag(const uint16_t* tile, int cb, int r0, int lane) {
+  const u32x2 lo = lds_read_tr16(tile + 16 * (R * cb + r0) + 4 * lane);
+  const u32x2 hi = lds_read_tr16(tile + 16 * (R * cb + r0 + 16) + 4 * lane);
+  const u32x4 v = {lo[0], lo[1], hi[0], hi[1]};
+  return as_bf16x8(v);
+}
+
+// B operand from two C-layout blocks (rows 4 lg + j of block 0, then of block 1)
+__device__ __forceinline__ bf16x8 pack_frag(const float (&x)[2][4]) {
+  const u32x4 v = {pack_bf16x2(x[0][0], x[0][1]), pack_bf16x2(x[0][2], x[0][3]), pack_bf16x2(x[1][0], x[1][1]),
+                   pack_bf16x2(x[1][2], x[1][3])};
+  return as_bf16x8(v);
+}
+
+__device__ __forceinline__ void store_bf16x4(void* p, f32x4 v, float s) {
+  const u32x2 w = {pack_bf16x2(v[0] * s, v[1] * s), pack_bf16x2(v[2] * s, v[3] * s)};
+  *reinterpret_cast<u32x2*>(p) = w;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// row-wise preparation: one wave per row, CPL consecutive channels per lane
+
+constexpr int kPrepThreads = 256;
+
+template <int D>
+__global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(BwdArgs a) {
+  constexpr int DV = 2 * D;
+  constexpr int CPL = DV / 64;
+  constexpr int WAVES = kPrepThreads / 64;
+  __shared__ float sdw[WAVES][DV];
+  __shared__ float sdl[WAVES];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float lam = *a.lambda;
+  const float sigma = a.out_scale;
+  const long long rows = (long long)a.BH * a.N;
+  float w[CPL], dw[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    w[i] = a.norm_w ? a.norm_w[lane * CPL + i] : 1.0f;
+    dw[i] = 0.f;
+  }
+  float dl = 0.f;
+  const uint16_t* dout = (const uint16_t*)a.dout;
+  uint16_t* dy_out = a.dy;
+  for (long long row = (long long)blockIdx.x * WAVES + wave; row < rows; row += (long long)gridDim.x * WAVES) {
+    const float* o1 = a.osave + row * DV + lane * CPL;
+    const float* o2 = a.osave + (rows + row) * DV + lane * CPL;
+    const uint16_t* go = dout + row * DV + lane * CPL;
+    float y[CPL], g[CPL], x1[CPL], x2[CPL], gd[CPL];
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      x1[i] = o1[i];
+      x2[i] = o2[i];
+      gd[i] = __builtin_bit_cast(float, (uint32_t)go[i] << 16);
+      y[i] = x1[i] - lam * x2[i];
+      ss += y[i] * y[i];
+    }
+    ss = wave_sum(ss);
+    const float ir = 1.0f / sqrtf(ss * (1.0f / DV) + a.eps);
+    float gy = 0.f;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      g[i] = sigma * w[i] * gd[i];
+      gy += g[i] * y[i];
+    }
+    gy = wave_sum(gy);
+    const float k3 = gy * ir * ir * ir * (1.0f / DV);
+    // delta_k is formed from dY as rounded to bf16, the dY the products
+    // dP = dY V^T see, so that dP - delta cancels where it should (a row
+    // with one visible key has dS = 0 exactly); dlambda uses the fp32 dY
+    float t1 = 0.f, t2 = 0.f, u2 = 0.f;
+    uint16_t* dyp = dy_out + row * DV + lane * CPL;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const float dyv = g[i] * ir - y[i] * k3;
+      const uint16_t hb = (uint16_t)(pack_bf16x2(dyv, 0.f) & 0xffffu);
+      const float dyr = __builtin_bit_cast(float, (uint32_t)hb << 16);
+      t1 += dyr * x1[i];
+      t2 += dyr * x2[i];
+      u2 += dyv * x2[i];
+      dyp[i] = hb;
+      dw[i] += sigma * gd[i] * y[i] * ir;
+    }
+    t1 = wave_sum(t1);
+    t2 = wave_sum(t2);
+    u2 = wave_sum(u2);
+    if (lane == 0) {
+      a.delta[row] = t1;
+      a.delta[rows + row] = -lam * t2;
+    }
+    dl -= u2;
+  }
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) sdw[wave][lane * CPL + i] = dw[i];
+  if (lane == 0) sdl[wave] = dl;
+  __syncthreads();
+  float* part = a.partial + (size_t)blockIdx.x * (DV + 1);
+  for (int c = threadIdx.x; c < DV; c += kPrepThreads) {
+    float s = 0.f;
+#pragma unroll
+    for (int v = 0; v < WAVES; ++v) s += sdw[v][c];
+    part[c] = s;
+  }
+  if (threadIdx.x == 0) {
+    float s = 0.f;
+#pragma unroll
+    for (int v = 0; v < WAVES; ++v) s += sdl[v];
+    part[DV] = s;
+  }
+}
+
+// fixed-order sums of the per-workgroup partials: dw [2d] and dlambda
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* __restrict__ partial, int nparts, int width,
+                                                         float* __restrict__ dweight, float* __restrict__ dlambda) {
+  for (int c = threadIdx.x; c < width; c += 256) {
+    float s = 0.f;
+    for (int p = 0; p < nparts; ++p) s += partial[(size_t)p * width + c];
+    if (c == width - 1)
+      dlambda[0] = s;
+    else
+      dweight[c] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: a workgroup owns 64 query rows of one head (4 waves x 16) and streams
+// 32-key tiles of K1, K2, V through LDS.  Per wave and tile:
+//   S_k^T (32 keys x 16 queries) = K_k Q_k^T, dP^T = V dY^T,
+//   dS_k^T from A_k^T = 2^(S_k^T c - lse_k), then dQ_k^T += K_k^T dS_k^T.
+
+constexpr int kDqRows = 64;
+constexpr int kDqKeys = 32;
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
+  constexpr int DV = 2 * D, KS = D / 32, KV = DV / 32, DB = D / 16, BN = kDqKeys;
+  __shared__ __attribute__((aligned(16))) uint16_t sk1[BN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sk2[BN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sv[BN * DV];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int N = a.N, BH = a.BH;
+  const int nqt = (N + kDqRows - 1) / kDqRows;
+  const int bh = blockIdx.x % BH;
+  const int qt = CAUSAL ? nqt - 1 - (int)(blockIdx.x / BH) : (int)(blockIdx.x / BH);
+  const int q0 = qt * kDqRows, qw = q0 + 16 * wave, q = qw + lr, qc = min(q, N - 1);
+  const size_t hb = (size_t)bh * (size_t)N;
+  const size_t nrows = (size_t)BH * (size_t)N;
+  const float c = a.c, lam = *a.lambda;
+
+  const uint16_t* Q1 = (const uint16_t*)a.q1 + hb * D;
+  const uint16_t* Q2 = (const uint16_t*)a.q2 + hb * D;
+  const uint16_t* K1 = (const uint16_t*)a.k1 + hb * D;
+  const uint16_t* K2 = (const uint16_t*)a.k2 + hb * D;
+  const uint16_t* V = (const uint16_t*)a.v + hb * DV;
+  const uint16_t* DY = a.dy + hb * DV;
+
+  bf16x8 qf1[KS], qf2[KS], dyf[KV];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    qf1[ks] = as_bf16x8(ld16(Q1 + (size_t)qc * D + 32 * ks + 8 * lg));
+    qf2[ks] = as_bf16x8(ld16(Q2 + (size_t)qc * D + 32 * ks + 8 * lg));
+  }
+#pragma unroll
+  for (int kv = 0; kv < KV; ++kv) dyf[kv] = as_bf16x8(ld16(DY + (size_t)qc * DV + 32 * kv + 8 * lg));
+  const float lse1 = a.lse[hb + qc], lse2 = a.lse[nrows + hb + qc];
+  const float dl1 = a.delta[hb + qc], dl2 = a.delta[nrows + hb + qc];
+
+  f32x4 dq1[DB], dq2[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    dq1[db] = zero_f32x4();
+    dq2[db] = zero_f32x4();
+  }
+  const int kend = CAUSAL ? min(N, q0 + kDqRows) : N;
+  const int nkt = (kend + BN - 1) / BN;
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int k0 = kt * BN;
+    __syncthreads();  // everybody is done with the previous tile
+    stage_tile<BN, D, 256>(sk1, K1, k0, N, tid);
+    stage_tile<BN, D, 256>(sk2, K2, k0, N, tid);
+    stage_tile<BN, DV, 256>(sv, V, k0, N, tid);
+    __syncthreads();
+    if (qw >= N || (CAUSAL && k0 > qw + 15)) continue;  // nothing visible to this wave
+
+    float g1[2][4], g2[2][4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x4 s1 = zero_f32x4(), s2 = zero_f32x4(), dp = zero_f32x4();
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        s1 = mfma16x16x32_bf16(as_bf16x8(ld16(sk1 + boff<BN>(16 * kb + lr, 32 * ks + 8 * lg))), qf1[ks], s1);
+        s2 = mfma16x16x32_bf16(as_bf16x8(ld16(sk2 + boff<BN>(16 * kb + lr, 32 * ks + 8 * lg))), qf2[ks], s2);
+      }
+#pragma unroll
+      for (int kv = 0; kv < KV; ++kv)
+        dp = mfma16x16x32_bf16(as_bf16x8(ld16(sv + boff<BN>(16 * kb + lr, 32 * kv + 8 * lg))), dyf[kv], dp);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int key = k0 + 16 * kb + 4 * lg + j;
+        const bool ok = key < N && q < N && (!CAUSAL || key <= q);
+        const float e1 = ok ? exp2_fast(s1[j] * c - lse1) : 0.f;
+        const float e2 = ok ? exp2_fast(s2[j] * c - lse2) : 0.f;
+        g1[kb][j] = e1 * (dp[j] - dl1);
+        g2[kb][j] = e2 * (-lam * dp[j] - dl2);
+      }
+    }
+    const bf16x8 b1 = pack_frag(g1), b2 = pack_frag(g2);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      dq1[db] = mfma16x16x32_bf16(tr_frag<BN>(sk1, db, 0, lane), b1, dq1[db]);
+      dq2[db] = mfma16x16x32_bf16(tr_frag<BN>(sk2, db, 0, lane), b2, dq2[db]);
+    }
+  }
+  if (q < N) {
+    const float s = 1.0f / sqrtf((float)D);
+    uint16_t* o1 = (uint16_t*)a.dq1 + (hb + q) * D;
+    uint16_t* o2 = (uint16_t*)a.dq2 + (hb + q) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      store_bf16x4(o1 + 16 * db + 4 * lg, dq1[db], s);
+      store_bf16x4(o2 + 16 * db + 4 * lg, dq2[db], s);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: a workgroup owns 64 keys of one head (4 waves x 16) and streams
+// 32-query tiles of Q1, Q2, dY (and the rows' lse, delta) through LDS.  Per
+// wave and tile: S_k (32 queries x 16 keys) = Q_k K_k^T, dP = dY V^T, then
+//   dV^T += dY^T (A1 - lambda A2),  dK_k^T += Q_k^T dS_k.
+
+constexpr int kDkvKeys = 64;
+constexpr int kDkvRows = 32;
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdArgs a) {
+  constexpr int DV = 2 * D, KS = D / 32, KV = DV / 32, DB = D / 16, CB = DV / 16, BQ = kDkvRows;
+  __shared__ __attribute__((aligned(16))) uint16_t sq1[BQ * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sq2[BQ * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sdy[BQ * DV];
+  __shared__ __attribute__((aligned(16))) float sst[4][BQ];  // lse1, lse2, delta1, delta2
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int N = a.N, BH = a.BH;
+  const int bh = blockIdx.x % BH;
+  const int kt = blockIdx.x / BH;  // causal: the first key tiles see the most queries
+  const int k0 = kt * kDkvKeys, kw = k0 + 16 * wave, kk = kw + lr, kc = min(kk, N - 1);
+  const size_t hb = (size_t)bh * (size_t)N;
+  const size_t nrows = (size_t)BH * (size_t)N;
+  const float c = a.c, lam = *a.lambda;
+
+  const uint16_t* Q1 = (const uint16_t*)a.q1 + hb * D;
+  const uint16_t* Q2 = (const uint16_t*)a.q2 + hb * D;
+  const uint16_t* K1 = (const uint16_t*)a.k1 + hb * D;
+  const uint16_t* K2 = (const uint16_t*)a.k2 + hb * D;
+  const uint16_t* V = (const uint16_t*)a.v + hb * DV;
+  const uint16_t* DY = a.dy + hb * DV;
+
+  bf16x8 kf1[KS], kf2[KS], vf[KV];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    kf1[ks] = as_bf16x8(ld16(K1 + (size_t)kc * D + 32 * ks + 8 * lg));
+    kf2[ks] = as_bf16x8(ld16(K2 + (size_t)kc * D + 32 * ks + 8 * lg));
+  }
+#pragma unroll
+  for (int kv = 0; kv < KV; ++kv) vf[kv] = as_bf16x8(ld16(V + (size_t)kc * DV + 32 * kv + 8 * lg));
+
+  f32x4 dk1[DB], dk2[DB], dv[CB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    dk1[db] = zero_f32x4();
+    dk2[db] = zero_f32x4();
+  }
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) dv[cb] = zero_f32x4();
+
+  const int nqt = (N + BQ - 1) / BQ;
+  for (int qt = CAUSAL ? k0 / BQ : 0; qt < nqt; ++qt) {
+    const int q0 = qt * BQ;
+    __syncthreads();  // everybody is done with the previous tile
+    stage_tile<BQ, D, 256>(sq1, Q1, q0, N, tid);
+    stage_tile<BQ, D, 256>(sq2, Q2, q0, N, tid);
+    stage_tile<BQ, DV, 256>(sdy, DY, q0, N, tid);
+    if (tid < 4 * BQ) {
+      const int which = tid / BQ, r = tid % BQ;
+      const size_t row = hb + (size_t)min(q0 + r, N - 1);
+      sst[which][r] = which < 2 ? a.lse[(size_t)which * nrows + row] : a.delta[(size_t)(which - 2) * nrows + row];
+    }
+    __syncthreads();
+    if (kw >= N || (CAUSAL && q0 + BQ - 1 < kw)) continue;  // nothing visible to this wave
+
+    float d1[2][4], gs1[2][4], gs2[2][4];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      f32x4 s1 = zero_f32x4(), s2 = zero_f32x4(), dp = zero_f32x4();
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        s1 = mfma16x16x32_bf16(as_bf16x8(ld16(sq1 + boff<BQ>(16 * qb + lr, 32 * ks + 8 * lg))), kf1[ks], s1);
+        s2 = mfma16x16x32_bf16(as_bf16x8(ld16(sq2 + boff<BQ>(16 * qb + lr, 32 * ks + 8 * lg))), kf2[ks], s2);
+      }
+#pragma unroll
+      for (int kv = 0; kv < KV; ++kv)
+        dp = mfma16x16x32_bf16(as_bf16x8(ld16(sdy + boff<BQ>(16 * qb + lr, 32 * kv + 8 * lg))), vf[kv], dp);
+      const f32x4 l1 = *reinterpret_cast<const f32x4*>(&sst[0][16 * qb + 4 * lg]);
+      const f32x4 l2 = *reinterpret_cast<const f32x4*>(&sst[1][16 * qb + 4 * lg]);
+      const f32x4 t1 = *reinterpret_cast<const f32x4*>(&sst[2][16 * qb + 4 * lg]);
+      const f32x4 t2 = *reinterpret_cast<const f32x4*>(&sst[3][16 * qb + 4 * lg]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int qi = q0 + 16 * qb + 4 * lg + j;
+        const bool ok = qi < N && kk < N && (!CAUSAL || kk <= qi);
+        const float e1 = ok ? exp2_fast(s1[j] * c - l1[j]) : 0.f;
+        const float e2 = ok ? exp2_fast(s2[j] * c - l2[j]) : 0.f;
+        d1[qb][j] = e1 - lam * e2;
+        gs1[qb][j] = e1 * (dp[j] - t1[j]);
+        gs2[qb][j] = e2 * (-lam * dp[j] - t2[j]);
+      }
+    }
+    const bf16x8 bd = pack_frag(d1), b1 = pack_frag(gs1), b2 = pack_frag(gs2);
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) dv[cb] = mfma16x16x32_bf16(tr_frag<BQ>(sdy, cb, 0, lane), bd, dv[cb]);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      dk1[db] = mfma16x16x32_bf16(tr_frag<BQ>(sq1, db, 0, lane), b1, dk1[db]);
+      dk2[db] = mfma16x16x32_bf16(tr_frag<BQ>(sq2, db, 0, lane), b2, dk2[db]);
+    }
+  }
+  if (kk < N) {
+    const float s = 1.0f / sqrtf((float)D);
+    uint16_t* o1 = (uint16_t*)a.dk1 + (hb + kk) * D;
+    uint16_t* o2 = (uint16_t*)a.dk2 + (hb + kk) * D;
+    uint16_t* ov = (uint16_t*)a.dv + (hb + kk) * DV;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      store_bf16x4(o1 + 16 * db + 4 * lg, dk1[db], s);
+      store_bf16x4(o2 + 16 * db + 4 * lg, dk2[db], s);
+    }
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) store_bf16x4(ov + 16 * cb + 4 * lg, dv[cb], 1.0f);
+  }
+}
+
+// Eq. 2 backward: dlq1 = dl e1 lk1, dlk1 = dl e1 lq1, dlq2 = -dl e2 lk2,
+// dlk2 = -dl e2 lq2 with e_k = exp(lqk . lkk).  One wave.
+__global__ __launch_bounds__(64) void lambda_bwd_kernel(const float* __restrict__ lq1, const float* __restrict__ lk1,
+                                                        const float* __restrict__ lq2, const float* __restrict__ lk2,
+                                                        int d, const float* __restrict__ dlambda,
+                                                        float* __restrict__ dlq1, float* __restrict__ dlk1,
+                                                        float* __restrict__ dlq2, float* __restrict__ dlk2) {
+  float x = 0.f, y = 0.f;
+  for (int i = threadIdx.x; i < d; i += 64) {
+    x += lq1[i] * lk1[i];
+    y += lq2[i] * lk2[i];
+  }
+  x = wave_sum(x);
+  y = wave_sum(y);
+  const float g = dlambda[0];
+  const float g1 = g * expf(x), g2 = -g * expf(y);
+  for (int i = threadIdx.x; i < d; i += 64) {
+    dlq1[i] = g1 * lk1[i];
+    dlk1[i] = g1 * lq1[i];
+    dlq2[i] = g2 * lk2[i];
+    dlk2[i] = g2 * lq2[i];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dispatch
+
+int bwd_prep_blocks(long long rows) {
+  const long long per = kPrepThreads / 64;
+  const long long need = (rows + per - 1) / per;
+  return (int)(need < 1024 ? (need > 0 ? need : 1) : 1024);
+}
+
+template <int D, bool C>
+static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
+  const long long rows = (long long)a.BH * a.N;
+  const int np = bwd_prep_blocks(rows);
+  hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3(np), dim3(kPrepThreads), 0, s, a);
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3(1), dim3(256), 0, s, a.partial, np, 2 * D + 1, a.dweight, a.dlambda);
+  const unsigned gq = (unsigned)(((a.N + kDqRows - 1) / kDqRows) * (long long)a.BH);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, C>), dim3(gq), dim3(256), 0, s, a);
+  const unsigned gk = (unsigned)(((a.N + kDkvKeys - 1) / kDkvKeys) * (long long)a.BH);
+  hipLaunchKernelGGL((bwd_dkv_kernel<D, C>), dim3(gk), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd(int d, bool causal, const BwdArgs& a, hipStream_t stream) {
+  switch (d) {
+    case 32: return causal ? launch_bwd_d<32, true>(a, stream) : launch_bwd_d<32, false>(a, stream);
+    case 64: return causal ? launch_bwd_d<64, true>(a, stream) : launch_bwd_d<64, false>(a, stream);
+    case 128: return causal ? launch_bwd_d<128, true>(a, stream) : launch_bwd_d<128, false>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_lambda_bwd(const float* lq1, const float* lk1, const float* lq2, const float* lk2, int d,
+                             const float* dlambda, float* dlq1, float* dlk1, float* dlq2, float* dlk2,
+                             hipStream_t stream) {
+  hipLaunchKernelGGL(lambda_bwd_kernel, dim3(1), dim3(64), 0, stream, lq1, lk1, lq2, lk2, d, dlambda, dlq1, dlk1,
+                     dlq2, dlk2);
+  return hipGetLastError();
+}
+
+}  // namespace diffattn

@@ -71,6 +71,21 @@ __device__ __forceinline__ f32x4 zero_f32x4() {
   return z;
 }
 
+// Transposing LDS read (ds_read_b64_tr_b16).  Each lane of a 16-lane group
+// supplies the address of 4 consecutive bf16 of one row; the group's 16 x 4
+// block comes back transposed.  With a tile stored as [16-column block][row]
+// [16 columns] and lane L pointing at element 16 (r0 + L / 4) + 4 (L % 4) of
+// a column block, lane L receives that block's column L % 16 for rows
+// r0 + 4 (L / 16) .. + 3 -- half of the A operand of a 16x16x32 MFMA whose
+// k runs over rows.
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+#define DIFFATTN_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+  s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(u32x2, r);
+}
+
 // 16-byte global load / store through plain pointers.
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }

@@ -21,6 +21,8 @@ struct PrefillArgs {
   const float* norm_w;  // device [2d] or null (ones)
   float eps;
   float c;              // log2(e) / sqrt(d)
+  float* lse;           // training forward: [2][BH][N] log2-sum-exp per map, or null
+  float* osave;         // training forward: [2][BH][N][2d] per-map O / l, or null
 };
 
 struct DecodeArgs {
@@ -42,6 +44,34 @@ struct DecodeArgs {
   float* ws;             // [B*H*S] records of (4 + 4d) floats
 };
 
+struct BwdArgs {
+  const void* q1;
+  const void* k1;
+  const void* q2;
+  const void* k2;
+  const void* v;
+  const void* dout;     // [BH][N][2d] gradient of the output
+  const float* lse;     // [2][BH][N] from the training forward (log2 units)
+  const float* osave;   // [2][BH][N][2d] per-map O / l from the training forward
+  void* dq1;
+  void* dk1;
+  void* dq2;
+  void* dk2;
+  void* dv;
+  float* dweight;       // [2d]
+  float* dlambda;       // [1]
+  uint16_t* dy;         // workspace: [BH][N][2d] bf16 gradient of Y
+  float* delta;         // workspace: [2][BH][N]
+  float* partial;       // workspace: [prep workgroups][2d + 1]
+  int BH;
+  int N;
+  const float* lambda;
+  float out_scale;      // 1 - lambda_init
+  const float* norm_w;  // [2d] or null (ones)
+  float eps;
+  float c;              // log2(e) / sqrt(d)
+};
+
 // Query rows and threads per workgroup of the prefill kernels.
 int prefill_block_rows(bool bf16, int d);
 int prefill_block_threads(bool bf16, int d);
@@ -57,5 +87,13 @@ void decode_plan(int B, int H, int L, int d, int* S, int* chunk);
 size_t decode_record_floats(int d);
 
 hipError_t launch_decode(bool bf16, int d, bool norm, const DecodeArgs& a, hipStream_t stream);
+
+// Backward: workgroups of the row-wise preparation kernel for `rows` rows
+// (each writes one partial record), and the launch of all four kernels.
+int bwd_prep_blocks(long long rows);
+hipError_t launch_bwd(int d, bool causal, const BwdArgs& a, hipStream_t stream);
+hipError_t launch_lambda_bwd(const float* lq1, const float* lk1, const float* lq2, const float* lk2, int d,
+                             const float* dlambda, float* dlq1, float* dlk1, float* dlq2, float* dlk2,
+                             hipStream_t stream);
 
 }  // namespace diffattn

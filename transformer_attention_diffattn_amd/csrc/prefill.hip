@@ -152,13 +152,6 @@ struct Bf16Tile {
   static __device__ __forceinline__ int kchunk(int r, int c) { return c ^ ((r / RPK) % NCH); }
 };
 
-typedef __attribute__((ext_vector_type(4))) short s16x4;
-#define DIFFATTN_LDS(p) ((__attribute__((address_space(3))) void*)(p))
-
-__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
-  s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
-  return __builtin_bit_cast(u32x2, r);
-}
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -719,6 +712,24 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
     int ln = lane;
     asm volatile("" : "+v"(ln));
     const int lr = ln & 15, lg = ln >> 4;
+    // Training forward: this map's per-row log-sum-exp (log2 units: m plus
+    // log2 of the row sum) and its normalised output O/l, kept for the
+    // backward.  Issued before the output stores, so the wait for the next
+    // tile (which leaves only those outstanding) also covers them.
+    if (a.osave) {
+#pragma unroll
+      for (int u = 0; u < SUB; ++u) {
+        const int row = it.qw0 + 16 * u + lr;
+        if (row < N) {
+          const size_t srow = (size_t)(MP * BH + it.bh) * (size_t)N + (size_t)row;
+          const float il = 1.0f / L[u][0];
+          if (lg == 0) a.lse[srow] = m[u] + log2f(L[u][0]);
+          float* op = a.osave + srow * DV + 4 * lg;
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) *reinterpret_cast<f32x4*>(op + 16 * cb) = O[u][cb] * il;
+        }
+      }
+    }
     // nb: the buffer of the next tile to consume (the next item's first)
     const int fb0 = nb == 0 ? STAGES - 1 : nb - 1;  // the buffer the last tile used
     const int fb1 = fb0 == 0 ? STAGES - 1 : fb0 - 1;
