@@ -174,8 +174,9 @@ diffattn_status diffattn_bwd(diffattn_dtype dt, const void* q1, const void* k1, 
   if (!ok_ptr4(lambda) || !ok_ptr4(dlambda) || !ok_ptr4(dweight)) return DIFFATTN_EINVAL;
   if (norm_weight && !aligned(norm_weight, 4)) return DIFFATTN_EINVAL;
   const long long BH = (long long)B * H;
-  // grids of (N / 64) x BH workgroups and row indices below 2^31 per head
-  if (BH > INT32_MAX || ((long long)N + 63) / 64 * BH > (long long)INT32_MAX) return DIFFATTN_EINVAL;
+  // grids of (N / 64) x BH workgroups; the kernels address a head's rows and
+  // the [2, B*H*N] statistics with 32-bit byte offsets
+  if (BH * N > (1LL << 28) || (long long)N * 4 * d >= (1LL << 32)) return DIFFATTN_EINVAL;
   size_t od, op, total;
   bwd_layout(B, H, N, d, &od, &op, &total);
   if (workspace == nullptr || workspace_bytes < total) return DIFFATTN_EWORKSPACE;

@@ -55,21 +55,19 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// Copy rows [r0, r0 + R) of a row-major [*, C] bf16 matrix (rows past
-// n_rows - 1 read row n_rows - 1) into an R x C blocked LDS tile.
-template <int R, int C, int NT>
-__device__ __forceinline__ void stage_tile(uint16_t* __restrict__ dst, const uint16_t* __restrict__ src, int r0,
-                                           int n_rows, int tid) {
-  constexpr int CH = R * C / 8;  // 16-byte chunks
-#pragma unroll
-  for (int i = 0; i < (CH + NT - 1) / NT; ++i) {
-    const int idx = tid + i * NT;
-    if (CH % NT == 0 || idx < CH) {
-      const int r = idx / (C / 8), c8 = idx % (C / 8);
-      const int gr = min(r0 + r, n_rows - 1);
-      st16(dst + boff<R>(r, 8 * c8), ld16(src + (size_t)gr * C + 8 * c8));
-    }
-  }
+// Tiles of 32 rows stream through a ring of LDS stage buffers by direct
+// global->LDS loads.  One load instruction moves 32 rows x 16 columns (one
+// column block, 1 KB) of a row-major [*, C] bf16 matrix: lane L fetches row
+// r0 + L / 2 (rows past n_rows - 1 read row n_rows - 1), columns
+// 16 cb + 8 (L % 2) .. + 7, which the blocked layout puts at byte 16 L of
+// the block -- the position the instruction writes lane L's 16 bytes to.
+constexpr int kTileRows = 32;
+constexpr int kStages = 3;
+
+__device__ __forceinline__ void dma_block(const uint16_t* src, int C, int cb, int r0, int n_rows, int lane,
+                                          uint32_t lds_block) {
+  const int r = min(r0 + (lane >> 1), n_rows - 1);
+  lds_dma16_s(src, (uint32_t)(r * C + 16 * cb + 8 * (lane & 1)) * 2u, lds_block);
 }
 
 // A operand with k over 32 rows starting at r0 of column block cb (R-row tile)
@@ -188,12 +186,15 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(BwdArgs a) {
   }
 }
 
-// fixed-order sums of the per-workgroup partials: dw [2d] and dlambda
-__global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* __restrict__ partial, int nparts, int width,
-                                                         float* __restrict__ dweight, float* __restrict__ dlambda) {
-  for (int c = threadIdx.x; c < width; c += 256) {
-    float s = 0.f;
-    for (int p = 0; p < nparts; ++p) s += partial[(size_t)p * width + c];
+// fixed-order sums of the per-workgroup partials, one wave per column:
+// dw [2d] (columns 0..2d-1) and dlambda (column 2d)
+__global__ __launch_bounds__(64) void bwd_reduce_kernel(const float* __restrict__ partial, int nparts, int width,
+                                                        float* __restrict__ dweight, float* __restrict__ dlambda) {
+  const int c = blockIdx.x;
+  float s = 0.f;
+  for (int p = threadIdx.x; p < nparts; p += 64) s += partial[(size_t)p * width + c];
+  s = wave_sum(s);
+  if (threadIdx.x == 0) {
     if (c == width - 1)
       dlambda[0] = s;
     else
@@ -213,9 +214,10 @@ constexpr int kDqKeys = 32;
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   constexpr int DV = 2 * D, KS = D / 32, KV = DV / 32, DB = D / 16, BN = kDqKeys;
-  __shared__ __attribute__((aligned(16))) uint16_t sk1[BN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sk2[BN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sv[BN * DV];
+  static_assert(BN == kTileRows, "one load instruction per 32-row column block");
+  constexpr int STAGE = 2 * BN * D + BN * DV;  // K1, K2, V tiles
+  constexpr int NI = D / 16;                   // load instructions per wave and tile
+  __shared__ __attribute__((aligned(16))) uint16_t stg[kStages * STAGE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   const int N = a.N, BH = a.BH;
@@ -253,13 +255,37 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   }
   const int kend = CAUSAL ? min(N, q0 + kDqRows) : N;
   const int nkt = (kend + BN - 1) / BN;
+  // segments of a stage: the D/16 column blocks of K1, then of K2, then
+  // the D/8 of V; wave w issues segments w, w + 4, ...
+  const uint32_t lds0 = lds_offset(stg);
+  auto issue = [&](int kt) {
+    const uint32_t base = lds0 + 2u * (uint32_t)((kt % kStages) * STAGE);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int sg = wave + 4 * i;
+      if (sg < D / 16)
+        dma_block(K1, D, sg, kt * BN, N, lane, base + 1024u * sg);
+      else if (sg < D / 8)
+        dma_block(K2, D, sg - D / 16, kt * BN, N, lane, base + 2u * BN * D + 1024u * (sg - D / 16));
+      else
+        dma_block(V, DV, sg - D / 8, kt * BN, N, lane, base + 4u * BN * D + 1024u * (sg - D / 8));
+    }
+  };
+  issue(0);
+  if (nkt > 1) issue(1);
   for (int kt = 0; kt < nkt; ++kt) {
     const int k0 = kt * BN;
-    __syncthreads();  // everybody is done with the previous tile
-    stage_tile<BN, D, 256>(sk1, K1, k0, N, tid);
-    stage_tile<BN, D, 256>(sk2, K2, k0, N, tid);
-    stage_tile<BN, DV, 256>(sv, V, k0, N, tid);
+    // tile kt has landed (only tile kt+1 may still load) for every wave, and
+    // everybody is done with tile kt-1, whose buffer tile kt+2 reuses
+    if (kt + 1 < nkt)
+      wait_vmem_keep<NI>();
+    else
+      wait_vmem();
     __syncthreads();
+    if (kt + 2 < nkt) issue(kt + 2);
+    const uint16_t* sk1 = stg + (kt % kStages) * STAGE;
+    const uint16_t* sk2 = sk1 + BN * D;
+    const uint16_t* sv = sk1 + 2 * BN * D;
     if (qw >= N || (CAUSAL && k0 > qw + 15)) continue;  // nothing visible to this wave
 
     float g1[2][4], g2[2][4];
@@ -315,10 +341,11 @@ constexpr int kDkvRows = 32;
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdArgs a) {
   constexpr int DV = 2 * D, KS = D / 32, KV = DV / 32, DB = D / 16, CB = DV / 16, BQ = kDkvRows;
-  __shared__ __attribute__((aligned(16))) uint16_t sq1[BQ * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sq2[BQ * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sdy[BQ * DV];
-  __shared__ __attribute__((aligned(16))) float sst[4][BQ];  // lse1, lse2, delta1, delta2
+  static_assert(BQ == kTileRows, "one load instruction per 32-row column block");
+  constexpr int STAGE = 2 * BQ * D + BQ * DV;  // Q1, Q2, dY tiles
+  constexpr int NI = D / 16;                   // tile load instructions per wave and tile
+  __shared__ __attribute__((aligned(16))) uint16_t stg[kStages * STAGE];
+  __shared__ __attribute__((aligned(16))) float sstat[kStages][4][BQ];  // lse1, lse2, delta1, delta2
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   const int N = a.N, BH = a.BH;
@@ -355,18 +382,54 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdArgs a) {
   for (int cb = 0; cb < CB; ++cb) dv[cb] = zero_f32x4();
 
   const int nqt = (N + BQ - 1) / BQ;
-  for (int qt = CAUSAL ? k0 / BQ : 0; qt < nqt; ++qt) {
+  const int qt0 = CAUSAL ? k0 / BQ : 0;
+  // segments of a stage: the D/16 column blocks of Q1, then of Q2, then the
+  // D/8 of dY; wave w issues segments w, w + 4, ...; waves 0 and 1 also
+  // load the rows' (lse1, lse2) and (delta1, delta2) pairs, one 4-byte
+  // value per lane (lanes 0-31 the first of the pair, 32-63 the second)
+  const uint32_t lds0 = lds_offset(stg);
+  const uint32_t lds_st = lds_offset(sstat);
+  auto issue = [&](int qt) {
+    const int q0 = qt * BQ, buf = qt % kStages;
+    const uint32_t base = lds0 + 2u * (uint32_t)(buf * STAGE);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int sg = wave + 4 * i;
+      if (sg < D / 16)
+        dma_block(Q1, D, sg, q0, N, lane, base + 1024u * sg);
+      else if (sg < D / 8)
+        dma_block(Q2, D, sg - D / 16, q0, N, lane, base + 2u * BQ * D + 1024u * (sg - D / 16));
+      else
+        dma_block(DY, DV, sg - D / 8, q0, N, lane, base + 4u * BQ * D + 1024u * (sg - D / 8));
+    }
+    if (wave < 2) {
+      // two rows of nrows apart: the byte offset stays below 2^32 because
+      // the host limits B * H * N to 2^28
+      const float* src = (wave == 0 ? a.lse : a.delta) + hb;
+      const uint32_t off = 4u * (uint32_t)((size_t)(lane >> 5) * nrows + (size_t)min(q0 + (lane & 31), N - 1));
+      lds_dma4_s(src, off, lds_st + 4u * (uint32_t)((buf * 4 + 2 * wave) * BQ));
+    }
+  };
+  issue(qt0);
+  if (qt0 + 1 < nqt) issue(qt0 + 1);
+  for (int qt = qt0; qt < nqt; ++qt) {
     const int q0 = qt * BQ;
-    __syncthreads();  // everybody is done with the previous tile
-    stage_tile<BQ, D, 256>(sq1, Q1, q0, N, tid);
-    stage_tile<BQ, D, 256>(sq2, Q2, q0, N, tid);
-    stage_tile<BQ, DV, 256>(sdy, DY, q0, N, tid);
-    if (tid < 4 * BQ) {
-      const int which = tid / BQ, r = tid % BQ;
-      const size_t row = hb + (size_t)min(q0 + r, N - 1);
-      sst[which][r] = which < 2 ? a.lse[(size_t)which * nrows + row] : a.delta[(size_t)(which - 2) * nrows + row];
+    // tile qt has landed (only tile qt+1 may still load) for every wave, and
+    // everybody is done with tile qt-1, whose buffer tile qt+2 reuses
+    if (qt + 1 < nqt) {
+      if (wave < 2)
+        wait_vmem_keep<NI + 1>();
+      else
+        wait_vmem_keep<NI>();
+    } else {
+      wait_vmem();
     }
     __syncthreads();
+    if (qt + 2 < nqt) issue(qt + 2);
+    const uint16_t* sq1 = stg + (qt % kStages) * STAGE;
+    const uint16_t* sq2 = sq1 + BQ * D;
+    const uint16_t* sdy = sq1 + 2 * BQ * D;
+    const float(*sst)[BQ] = sstat[qt % kStages];
     if (kw >= N || (CAUSAL && q0 + BQ - 1 < kw)) continue;  // nothing visible to this wave
 
     float d1[2][4], gs1[2][4], gs2[2][4];
@@ -458,7 +521,7 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
   const long long rows = (long long)a.BH * a.N;
   const int np = bwd_prep_blocks(rows);
   hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3(np), dim3(kPrepThreads), 0, s, a);
-  hipLaunchKernelGGL(bwd_reduce_kernel, dim3(1), dim3(256), 0, s, a.partial, np, 2 * D + 1, a.dweight, a.dlambda);
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3(2 * D + 1), dim3(64), 0, s, a.partial, np, 2 * D + 1, a.dweight, a.dlambda);
   const unsigned gq = (unsigned)(((a.N + kDqRows - 1) / kDqRows) * (long long)a.BH);
   hipLaunchKernelGGL((bwd_dq_kernel<D, C>), dim3(gq), dim3(256), 0, s, a);
   const unsigned gk = (unsigned)(((a.N + kDkvKeys - 1) / kDkvKeys) * (long long)a.BH);

@@ -86,6 +86,46 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, r);
 }
 
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Byte offset of an LDS location (wave-uniform callers only).
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)DIFFATTN_LDS(p));
+}
+
+// 16 bytes per lane from global memory straight into LDS at lds + 16*lane
+// (global_load_lds_dwordx4).  Issued through asm so that the compiler does
+// not track it: it would otherwise wait for every outstanding tile before
+// any LDS read.  Completion is awaited explicitly with s_waitcnt vmcnt plus
+// a workgroup barrier before the data is read.
+__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds) : "memory", "m0");
+}
+// The same with a wave-uniform 64-bit base (scalar registers) and a 32-bit
+// per-lane byte offset.
+__device__ __forceinline__ void lds_dma16_s(const void* base, uint32_t off, uint32_t lds) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  const uint64_t ub = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t ul = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(ub), "s"(ul) : "memory", "m0");
+}
+// wait until at most K vector-memory operations of this wave are outstanding
+template <int K>
+__device__ __forceinline__ void wait_vmem_keep() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(K) : "memory");
+}
+// 4 bytes per lane straight into LDS at lds + 4*lane (global_load_lds_dword),
+// with a wave-uniform base and a per-lane byte offset; tracked like the
+// 16-byte form.
+__device__ __forceinline__ void lds_dma4_s(const void* base, uint32_t off, uint32_t lds) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  const uint64_t ub = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t ul = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(ub), "s"(ul) : "memory", "m0");
+}
+
 // 16-byte global load / store through plain pointers.
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }

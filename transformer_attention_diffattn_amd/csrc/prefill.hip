@@ -153,36 +153,6 @@ struct Bf16Tile {
 };
 
 
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// Byte offset of an LDS location (wave-uniform callers only).
-__device__ __forceinline__ uint32_t lds_offset(const void* p) {
-  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)DIFFATTN_LDS(p));
-}
-
-// 16 bytes per lane from global memory straight into LDS at lds + 16*lane
-// (global_load_lds_dwordx4).  Issued through asm so that the compiler does
-// not track it: it would otherwise wait for every outstanding tile before
-// any LDS read.  Completion is awaited explicitly with s_waitcnt vmcnt plus
-// a workgroup barrier before the data is read.
-__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds) : "memory", "m0");
-}
-// The same with a wave-uniform 64-bit base (scalar registers) and a 32-bit
-// per-lane byte offset.
-__device__ __forceinline__ void lds_dma16_s(const void* base, uint32_t off, uint32_t lds) {
-  const uint64_t b = (uint64_t)(uintptr_t)base;
-  const uint64_t ub = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
-                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
-  const uint32_t ul = __builtin_amdgcn_readfirstlane(lds);
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(ub), "s"(ul) : "memory", "m0");
-}
-// wait until at most K vector-memory operations of this wave are outstanding
-template <int K>
-__device__ __forceinline__ void wait_vmem_keep() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(K) : "memory");
-}
-
 // v_max_f32 as such: the operands here are never NaN (scores, or -inf
 // where masked), so the quieting copies fmaxf would add are not needed
 __device__ __forceinline__ float max_f32(float a, float b) {
