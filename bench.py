@@ -8,7 +8,8 @@ the whole-step throughput in TFLOP/s (12 d flops per causal query/key pair),
 the prefill kernel's roofline fraction against the bf16 dense MFMA peak, the
 CPU fp64 oracle timed on a bounded sample of the same workload, and a decode
 leg (diffattn_decode on 64 sequences x 16 heads x 32768 cached keys, d=128)
-reported in HBM GB/s against the 8 TB/s peak.  Inputs are seeded synthetic
+reported in HBM GB/s against the 8 TB/s peak, and a training leg
+(diffattn_fwd_train + diffattn_bwd on the prefill workload).  Inputs are seeded synthetic
 tensors already resident in HBM when timing starts.  The prefill step is
 replayed from a HIP graph (checked equal to the eager step) so that host
 launch overhead does not idle the GPU; kernel durations come from HIP events
@@ -148,6 +149,87 @@ def reference_gemm(torch, dev, n: int = 8192, seconds: float = 0.5):
     return 2.0 * n ** 3 / (ms * 1e-3) / 1e12
 
 
+def backward_leg(x, w, args, stream, torch, da):
+    """diffattn_fwd_train and diffattn_bwd on the same workload, each replayed
+    from a HIP graph (checked equal to the eager call).  The backward is priced
+    at its algorithmic 20 d flops per causal pair (two QK^T products 4 d, dP 4 d,
+    dV 4 d, dK1 + dK2 4 d, dQ1 + dQ2 4 d); the kernels execute 28 d, because
+    the query-parallel dQ kernel evaluates S and dP again."""
+    dev = x["q1"].device
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed + 7)
+    dout = torch.randn(x["v"].shape, generator=gen, device=dev).to(torch.bfloat16)
+    lam_t = da.lam(x["lq1"], x["lk1"], x["lq2"], x["lk2"], x["lambda_init"])
+    ws = torch.empty(da.bwd_workspace_bytes(w.B, w.H, w.N, w.d), dtype=torch.uint8, device=dev)
+    _, lse, o12 = da.fwd_train(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam_t, x["lambda_init"],
+                               eps=x["eps"], causal=w.causal)
+    grads = da.bwd(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], dout, lse, o12, lam_t, x["lambda_init"],
+                   eps=x["eps"], causal=w.causal, workspace=ws)
+    torch.cuda.synchronize()
+    eager = {k: v.clone() for k, v in grads.items()}
+
+    def bstep():
+        da.bwd(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], dout, lse, o12, lam_t, x["lambda_init"],
+               eps=x["eps"], causal=w.causal, workspace=ws, grads=grads)
+
+    def fstep():
+        da.fwd_train(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam_t, x["lambda_init"], eps=x["eps"],
+                     causal=w.causal)
+
+    R = 10
+    n = max(R, args.bwd_steps // R * R)
+    g_b = _graph(lambda: [bstep() for _ in range(R)], torch)
+    _prewarm(g_b.replay, min(0.5, args.prewarm_s), torch)
+    bms = _timed(g_b.replay, n // R, stream, torch) / n
+    for k, v in grads.items():
+        if not torch.equal(v, eager[k]):
+            raise RuntimeError(f"graph replay of the backward differs from the eager call ({k})")
+    g_f = _graph(lambda: [fstep() for _ in range(R)], torch)
+    _prewarm(g_f.replay, min(0.3, args.prewarm_s), torch)
+    fms = _timed(g_f.replay, n // R, stream, torch) / n
+    flops = 20.0 * w.d * w.pairs() * w.B * w.H
+    achieved = flops / (bms * 1e-3) / 1e12
+    leg = {
+        "workload": w.name, "ms_per_step": round(bms, 4), "flops_per_pair": 20 * w.d,
+        "executed_flops_per_pair": 28 * w.d, "tflops": round(achieved, 2),
+        "fwd_train_ms": round(fms, 4),
+        "fwd_train_tflops": round(12.0 * w.d * w.pairs() * w.B * w.H / (fms * 1e-3) / 1e12, 2),
+        "roofline": {"bound": "mfma", "kernel": "bwd_prep + bwd_reduce + bwd_dq + bwd_dkv <64,causal>",
+                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": _traffic("backward_layer1p4b", "backward.hip")},
+    }
+    if not args.no_cpu:
+        leg["cpu_baseline"] = cpu_backward(x, w, dout, budget_s=5.0)
+    return leg
+
+
+def cpu_backward(x, w, dout, budget_s: float):
+    """The oracle's backward as it stands, on whole heads of the same inputs,
+    until ``budget_s`` seconds are spent; priced at 20 d flops per pair."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import diffattn_oracle as O
+
+    done = 0
+    t0 = time.perf_counter()
+    for b in range(w.B):
+        for h in range(w.H):
+            sl = lambda t: t[b:b + 1, h:h + 1].cpu()
+            O.backward(sl(x["q1"]), sl(x["k1"]), sl(x["q2"]), sl(x["k2"]), sl(x["v"]), x["lq1"].cpu(),
+                       x["lk1"].cpu(), x["lq2"].cpu(), x["lk2"].cpu(), x["lambda_init"], sl(dout), eps=x["eps"],
+                       causal=w.causal)
+            done += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": 20.0 * w.d * w.pairs() * done / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "sample": f"{done} of {w.B * w.H} heads, dense fp64 NumPy, {dt:.1f} s wall"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -158,6 +240,8 @@ def main():
                          "core clock only after some time under load")
     ap.add_argument("--decode-steps", type=int, default=10)
     ap.add_argument("--no-decode", action="store_true", help="skip the decode leg")
+    ap.add_argument("--no-bwd", action="store_true", help="skip the training (backward) leg")
+    ap.add_argument("--bwd-steps", type=int, default=40)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of CPU oracle time")
     ap.add_argument("--no-ref-gemm", action="store_true",
@@ -279,6 +363,10 @@ def main():
                          "algorithmic_bytes": nbytes, "kernel_ms": round(dms, 4)},
         }
         del y, ws
+
+    # ---------------- training leg: forward with saved statistics + backward
+    if not args.no_bwd:
+        res["backward"] = backward_leg(x, w, args, stream, torch, da)
 
     if not args.no_ref_gemm:
         g = reference_gemm(torch, dev)

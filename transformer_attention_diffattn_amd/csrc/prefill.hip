@@ -171,7 +171,8 @@ __device__ __forceinline__ float max4_groups(float x) {
   return max_f32(u32_as_f32(q[0]), u32_as_f32(q[1]));
 }
 
-template <int D, bool CAUSAL, bool NORM>
+// SAVE: the training forward (also writes the per-map statistics).
+template <int D, bool CAUSAL, bool NORM, bool SAVE>
 __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(PrefillArgs a) {
   using T = Bf16Tile<D>;
   constexpr int DV = T::DV, BN = T::BN, KS = T::KS, NB = T::NB, NC = T::NC, CB = T::CB, SUB = T::SUB;
@@ -686,7 +687,7 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
     // log2 of the row sum) and its normalised output O/l, kept for the
     // backward.  Issued before the output stores, so the wait for the next
     // tile (which leaves only those outstanding) also covers them.
-    if (a.osave) {
+    if constexpr (SAVE) {
 #pragma unroll
       for (int u = 0; u < SUB; ++u) {
         const int row = it.qw0 + 16 * u + lr;
@@ -1169,7 +1170,7 @@ static hipError_t compute_units(int* ncu) {
   return e;
 }
 
-template <int D, bool C, bool NM>
+template <int D, bool C, bool NM, bool SV>
 static hipError_t launch_one(bool bf16, const PrefillArgs& a, hipStream_t s) {
   const long long items = (long long)a.n_qtiles * (long long)a.BH;
   const dim3 block(prefill_block_threads(bf16, D));
@@ -1179,26 +1180,39 @@ static hipError_t launch_one(bool bf16, const PrefillArgs& a, hipStream_t s) {
     const hipError_t e = compute_units(&ncu);
     if (e != hipSuccess) return e;
     const long long grid = items < ncu ? items : (ncu > 0 ? ncu : 1);
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, C, NM>), dim3((unsigned)grid), block, 0, s, a);
-  } else {
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, C, NM, SV>), dim3((unsigned)grid), block, 0, s, a);
+  } else if constexpr (!SV) {
     hipLaunchKernelGGL((prefill_f32_kernel<D, C, NM>), dim3((unsigned)items), block, 0, s, a);
+  } else {
+    return hipErrorInvalidValue;  // no fp32 training forward
   }
   return hipGetLastError();
 }
 
 template <int D>
-static hipError_t launch_d(bool bf16, bool causal, bool norm, const PrefillArgs& a, hipStream_t s) {
-  if (causal) return norm ? launch_one<D, true, true>(bf16, a, s) : launch_one<D, true, false>(bf16, a, s);
-  return norm ? launch_one<D, false, true>(bf16, a, s) : launch_one<D, false, false>(bf16, a, s);
+static hipError_t launch_d(bool bf16, bool causal, bool norm, bool save, const PrefillArgs& a, hipStream_t s) {
+  if constexpr (D >= 32) {
+    // the training forward: bf16, normalised output
+    if (save) {
+      if (!bf16 || !norm) return hipErrorInvalidValue;
+      return causal ? launch_one<D, true, true, true>(bf16, a, s) : launch_one<D, false, true, true>(bf16, a, s);
+    }
+  } else {
+    if (save) return hipErrorInvalidValue;
+  }
+  if (causal)
+    return norm ? launch_one<D, true, true, false>(bf16, a, s) : launch_one<D, true, false, false>(bf16, a, s);
+  return norm ? launch_one<D, false, true, false>(bf16, a, s) : launch_one<D, false, false, false>(bf16, a, s);
 }
 
 hipError_t launch_prefill(bool bf16, int d, bool causal, bool norm, const PrefillArgs& a,
                           hipStream_t stream) {
+  const bool save = a.osave != nullptr;
   switch (d) {
-    case 16: return launch_d<16>(bf16, causal, norm, a, stream);
-    case 32: return launch_d<32>(bf16, causal, norm, a, stream);
-    case 64: return launch_d<64>(bf16, causal, norm, a, stream);
-    case 128: return launch_d<128>(bf16, causal, norm, a, stream);
+    case 16: return launch_d<16>(bf16, causal, norm, save, a, stream);
+    case 32: return launch_d<32>(bf16, causal, norm, save, a, stream);
+    case 64: return launch_d<64>(bf16, causal, norm, save, a, stream);
+    case 128: return launch_d<128>(bf16, causal, norm, save, a, stream);
     default: return hipErrorInvalidValue;
   }
 }
