@@ -129,3 +129,65 @@ def test_decode_validation(L):
         assert _dec(L, ptrs=p) == b.EINVAL
     assert _dec(L, B=0) == b.OK
     assert _dec(L, B=70000) == b.EINVAL
+
+
+def _fwd_train(L, dt=b.BF16, d=64, B=1, H=1, N=8, flags=b.CAUSAL, lse=A16, o12=A16, ptrs=(A16,) * 6):
+    return L.diffattn_fwd_train(dt, *ptrs, B, H, N, d, A16, 0.8, None, 1e-5, flags, lse, o12, None)
+
+
+def test_fwd_train_validation(L):
+    assert _fwd_train(L, dt=b.FP32) == b.EUNSUPPORTED  # training takes bf16 only
+    for d in (16, 48, 256):
+        assert _fwd_train(L, d=d) == b.EUNSUPPORTED
+    assert _fwd_train(L, flags=b.CAUSAL | b.NO_NORM) == b.EINVAL
+    assert _fwd_train(L, lse=None) == b.EINVAL
+    assert _fwd_train(L, o12=A16 + 4) == b.EINVAL
+    assert _fwd_train(L, ptrs=(A16, A16, MIS, A16, A16, A16)) == b.EINVAL
+    assert _fwd_train(L, N=-1) == b.EINVAL
+    assert _fwd_train(L, N=0, lse=None, o12=None) == b.OK
+
+
+def test_bwd_workspace_bytes(L):
+    assert L.diffattn_bwd_workspace_bytes(0, 1, 8, 64) == 0
+    assert L.diffattn_bwd_workspace_bytes(1, 1, 8, 16) == 0
+    n = L.diffattn_bwd_workspace_bytes(4, 16, 2048, 64)
+    # at least dY (bf16) and the two delta rows
+    assert n >= 4 * 16 * 2048 * (128 * 2 + 2 * 4) and n % 256 == 0
+
+
+def _bwd(L, dt=b.BF16, d=64, B=1, H=1, N=8, flags=b.CAUSAL, ws=0x200000, wsb=1 << 24, ptrs=(A16,) * 13,
+         lam=A16, dlam=A16, dw=A16, eps=1e-5):
+    q1, k1, q2, k2, v, dout, lse, o12, dq1, dk1, dq2, dk2, dv = ptrs
+    return L.diffattn_bwd(dt, q1, k1, q2, k2, v, dout, lse, o12, B, H, N, d, lam, 0.8, None, eps, flags,
+                          dq1, dk1, dq2, dk2, dv, dlam, dw, ws, wsb, None)
+
+
+def test_bwd_validation(L):
+    assert _bwd(L, dt=b.FP32) == b.EUNSUPPORTED
+    assert _bwd(L, d=16) == b.EUNSUPPORTED
+    assert _bwd(L, flags=b.NO_NORM) == b.EINVAL
+    assert _bwd(L, eps=-1.0) == b.EINVAL
+    assert _bwd(L, B=-1) == b.EINVAL
+    for i in range(13):
+        p = [A16] * 13
+        p[i] = MIS
+        assert _bwd(L, ptrs=p) == b.EINVAL, i
+        p[i] = None
+        assert _bwd(L, ptrs=p) == b.EINVAL, i
+    assert _bwd(L, dlam=None) == b.EINVAL
+    assert _bwd(L, dw=A16 + 2) == b.EINVAL
+    assert _bwd(L, ws=None) == b.EWORKSPACE
+    assert _bwd(L, wsb=256) == b.EWORKSPACE
+    assert _bwd(L, ws=0x200000 + 16) == b.EINVAL  # the workspace must be 256-byte aligned
+    # sizes whose 32-bit row offsets would overflow
+    assert _bwd(L, B=1 << 12, H=1 << 12, N=1 << 6) == b.EINVAL
+    assert _bwd(L, N=0) == b.OK
+
+
+def test_lambda_bwd_validation(L):
+    p = [A16] * 9
+    for i in range(9):
+        q = list(p)
+        q[i] = None
+        assert L.diffattn_lambda_bwd(*q[:4], 64, *q[4:], None) == b.EINVAL
+    assert L.diffattn_lambda_bwd(*p[:4], 0, *p[4:], None) == b.EINVAL
