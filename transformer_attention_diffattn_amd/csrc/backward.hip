@@ -203,17 +203,24 @@ __global__ __launch_bounds__(64) void bwd_reduce_kernel(const float* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// dQ: a workgroup owns 64 query rows of one head (4 waves x 16) and streams
+// dQ: a workgroup owns 4 x 16 x SUB query rows of one head (4 waves) and streams
 // 32-key tiles of K1, K2, V through LDS.  Per wave and tile:
 //   S_k^T (32 keys x 16 queries) = K_k Q_k^T, dP^T = V dY^T,
 //   dS_k^T from A_k^T = 2^(S_k^T c - lse_k), then dQ_k^T += K_k^T dS_k^T.
 
-constexpr int kDqRows = 64;
 constexpr int kDqKeys = 32;
+// 16-row sub-tiles per wave: two where registers allow (d <= 64), so that
+// every K and V fragment read from LDS feeds two matrix products
+template <int D>
+struct DqCfg {
+  static constexpr int SUB = D <= 64 ? 2 : 1;
+  static constexpr int ROWS = 4 * 16 * SUB;  // query rows per workgroup
+};
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   constexpr int DV = 2 * D, KS = D / 32, KV = DV / 32, DB = D / 16, BN = kDqKeys;
+  constexpr int SUB = DqCfg<D>::SUB, ROWS = DqCfg<D>::ROWS;
   static_assert(BN == kTileRows, "one load instruction per 32-row column block");
   constexpr int STAGE = 2 * BN * D + BN * DV;  // K1, K2, V tiles
   constexpr int NI = D / 16;                   // load instructions per wave and tile
@@ -221,10 +228,10 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   const int N = a.N, BH = a.BH;
-  const int nqt = (N + kDqRows - 1) / kDqRows;
+  const int nqt = (N + ROWS - 1) / ROWS;
   const int bh = blockIdx.x % BH;
   const int qt = CAUSAL ? nqt - 1 - (int)(blockIdx.x / BH) : (int)(blockIdx.x / BH);
-  const int q0 = qt * kDqRows, qw = q0 + 16 * wave, q = qw + lr, qc = min(q, N - 1);
+  const int q0 = qt * ROWS, qw = q0 + 16 * SUB * wave;
   const size_t hb = (size_t)bh * (size_t)N;
   const size_t nrows = (size_t)BH * (size_t)N;
   const float c = a.c, lam = *a.lambda;
@@ -236,24 +243,37 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   const uint16_t* V = (const uint16_t*)a.v + hb * DV;
   const uint16_t* DY = a.dy + hb * DV;
 
-  bf16x8 qf1[KS], qf2[KS], dyf[KV];
+  // per sub-tile u: this lane's query, its Q / dY rows (B operands) and
+  // its row statistics
+  int q[SUB];
+  bf16x8 qf1[SUB][KS], qf2[SUB][KS], dyf[SUB][KV];
+  float lse1[SUB], lse2[SUB], dl1[SUB], dl2[SUB];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    qf1[ks] = as_bf16x8(ld16(Q1 + (size_t)qc * D + 32 * ks + 8 * lg));
-    qf2[ks] = as_bf16x8(ld16(Q2 + (size_t)qc * D + 32 * ks + 8 * lg));
+  for (int u = 0; u < SUB; ++u) {
+    q[u] = qw + 16 * u + lr;
+    const int qc = min(q[u], N - 1);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qf1[u][ks] = as_bf16x8(ld16(Q1 + (size_t)qc * D + 32 * ks + 8 * lg));
+      qf2[u][ks] = as_bf16x8(ld16(Q2 + (size_t)qc * D + 32 * ks + 8 * lg));
+    }
+#pragma unroll
+    for (int kv = 0; kv < KV; ++kv) dyf[u][kv] = as_bf16x8(ld16(DY + (size_t)qc * DV + 32 * kv + 8 * lg));
+    lse1[u] = a.lse[hb + qc];
+    lse2[u] = a.lse[nrows + hb + qc];
+    dl1[u] = a.delta[hb + qc];
+    dl2[u] = a.delta[nrows + hb + qc];
   }
-#pragma unroll
-  for (int kv = 0; kv < KV; ++kv) dyf[kv] = as_bf16x8(ld16(DY + (size_t)qc * DV + 32 * kv + 8 * lg));
-  const float lse1 = a.lse[hb + qc], lse2 = a.lse[nrows + hb + qc];
-  const float dl1 = a.delta[hb + qc], dl2 = a.delta[nrows + hb + qc];
 
-  f32x4 dq1[DB], dq2[DB];
+  f32x4 dq1[SUB][DB], dq2[SUB][DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    dq1[db] = zero_f32x4();
-    dq2[db] = zero_f32x4();
-  }
-  const int kend = CAUSAL ? min(N, q0 + kDqRows) : N;
+  for (int u = 0; u < SUB; ++u)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      dq1[u][db] = zero_f32x4();
+      dq2[u][db] = zero_f32x4();
+    }
+  const int kend = CAUSAL ? min(N, q0 + ROWS) : N;
   const int nkt = (kend + BN - 1) / BN;
   // segments of a stage: the D/16 column blocks of K1, then of K2, then
   // the D/8 of V; wave w issues segments w, w + 4, ...
@@ -286,45 +306,69 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
     const uint16_t* sk1 = stg + (kt % kStages) * STAGE;
     const uint16_t* sk2 = sk1 + BN * D;
     const uint16_t* sv = sk1 + 2 * BN * D;
-    if (qw >= N || (CAUSAL && k0 > qw + 15)) continue;  // nothing visible to this wave
+    if (qw >= N || (CAUSAL && k0 > qw + 16 * SUB - 1)) continue;  // nothing visible to this wave
 
-    float g1[2][4], g2[2][4];
+    float g1[SUB][2][4], g2[SUB][2][4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      f32x4 s1 = zero_f32x4(), s2 = zero_f32x4(), dp = zero_f32x4();
+      f32x4 s1[SUB], s2[SUB], dp[SUB];
+#pragma unroll
+      for (int u = 0; u < SUB; ++u) s1[u] = s2[u] = dp[u] = zero_f32x4();
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        s1 = mfma16x16x32_bf16(as_bf16x8(ld16(sk1 + boff<BN>(16 * kb + lr, 32 * ks + 8 * lg))), qf1[ks], s1);
-        s2 = mfma16x16x32_bf16(as_bf16x8(ld16(sk2 + boff<BN>(16 * kb + lr, 32 * ks + 8 * lg))), qf2[ks], s2);
+        const bf16x8 a1 = as_bf16x8(ld16(sk1 + boff<BN>(16 * kb + lr, 32 * ks + 8 * lg)));
+        const bf16x8 a2 = as_bf16x8(ld16(sk2 + boff<BN>(16 * kb + lr, 32 * ks + 8 * lg)));
+#pragma unroll
+        for (int u = 0; u < SUB; ++u) {
+          s1[u] = mfma16x16x32_bf16(a1, qf1[u][ks], s1[u]);
+          s2[u] = mfma16x16x32_bf16(a2, qf2[u][ks], s2[u]);
+        }
       }
 #pragma unroll
-      for (int kv = 0; kv < KV; ++kv)
-        dp = mfma16x16x32_bf16(as_bf16x8(ld16(sv + boff<BN>(16 * kb + lr, 32 * kv + 8 * lg))), dyf[kv], dp);
+      for (int kv = 0; kv < KV; ++kv) {
+        const bf16x8 av = as_bf16x8(ld16(sv + boff<BN>(16 * kb + lr, 32 * kv + 8 * lg)));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int key = k0 + 16 * kb + 4 * lg + j;
-        const bool ok = key < N && q < N && (!CAUSAL || key <= q);
-        const float e1 = ok ? exp2_fast(s1[j] * c - lse1) : 0.f;
-        const float e2 = ok ? exp2_fast(s2[j] * c - lse2) : 0.f;
-        g1[kb][j] = e1 * (dp[j] - dl1);
-        g2[kb][j] = e2 * (-lam * dp[j] - dl2);
+        for (int u = 0; u < SUB; ++u) dp[u] = mfma16x16x32_bf16(av, dyf[u][kv], dp[u]);
       }
+#pragma unroll
+      for (int u = 0; u < SUB; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int key = k0 + 16 * kb + 4 * lg + j;
+          const bool ok = key < N && q[u] < N && (!CAUSAL || key <= q[u]);
+          const float e1 = ok ? exp2_fast(s1[u][j] * c - lse1[u]) : 0.f;
+          const float e2 = ok ? exp2_fast(s2[u][j] * c - lse2[u]) : 0.f;
+          g1[u][kb][j] = e1 * (dp[u][j] - dl1[u]);
+          g2[u][kb][j] = e2 * (-lam * dp[u][j] - dl2[u]);
+        }
     }
-    const bf16x8 b1 = pack_frag(g1), b2 = pack_frag(g2);
+    bf16x8 b1[SUB], b2[SUB];
+#pragma unroll
+    for (int u = 0; u < SUB; ++u) {
+      b1[u] = pack_frag(g1[u]);
+      b2[u] = pack_frag(g2[u]);
+    }
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      dq1[db] = mfma16x16x32_bf16(tr_frag<BN>(sk1, db, 0, lane), b1, dq1[db]);
-      dq2[db] = mfma16x16x32_bf16(tr_frag<BN>(sk2, db, 0, lane), b2, dq2[db]);
+      const bf16x8 t1 = tr_frag<BN>(sk1, db, 0, lane), t2 = tr_frag<BN>(sk2, db, 0, lane);
+#pragma unroll
+      for (int u = 0; u < SUB; ++u) {
+        dq1[u][db] = mfma16x16x32_bf16(t1, b1[u], dq1[u][db]);
+        dq2[u][db] = mfma16x16x32_bf16(t2, b2[u], dq2[u][db]);
+      }
     }
   }
-  if (q < N) {
-    const float s = 1.0f / sqrtf((float)D);
-    uint16_t* o1 = (uint16_t*)a.dq1 + (hb + q) * D;
-    uint16_t* o2 = (uint16_t*)a.dq2 + (hb + q) * D;
+  const float s = 1.0f / sqrtf((float)D);
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      store_bf16x4(o1 + 16 * db + 4 * lg, dq1[db], s);
-      store_bf16x4(o2 + 16 * db + 4 * lg, dq2[db], s);
+  for (int u = 0; u < SUB; ++u) {
+    if (q[u] < N) {
+      uint16_t* o1 = (uint16_t*)a.dq1 + (hb + q[u]) * D;
+      uint16_t* o2 = (uint16_t*)a.dq2 + (hb + q[u]) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        store_bf16x4(o1 + 16 * db + 4 * lg, dq1[u][db], s);
+        store_bf16x4(o2 + 16 * db + 4 * lg, dq2[u][db], s);
+      }
     }
   }
 }
@@ -522,7 +566,7 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
   const int np = bwd_prep_blocks(rows);
   hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3(np), dim3(kPrepThreads), 0, s, a);
   hipLaunchKernelGGL(bwd_reduce_kernel, dim3(2 * D + 1), dim3(64), 0, s, a.partial, np, 2 * D + 1, a.dweight, a.dlambda);
-  const unsigned gq = (unsigned)(((a.N + kDqRows - 1) / kDqRows) * (long long)a.BH);
+  const unsigned gq = (unsigned)(((a.N + DqCfg<D>::ROWS - 1) / DqCfg<D>::ROWS) * (long long)a.BH);
   hipLaunchKernelGGL((bwd_dq_kernel<D, C>), dim3(gq), dim3(256), 0, s, a);
   const unsigned gk = (unsigned)(((a.N + kDkvKeys - 1) / kDkvKeys) * (long long)a.BH);
   hipLaunchKernelGGL((bwd_dkv_kernel<D, C>), dim3(gk), dim3(256), 0, s, a);
