@@ -94,81 +94,118 @@ __device__ __forceinline__ void store_bf16x4(void* p, f32x4 v, float s) {
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// row-wise preparation: one wave per row, CPL consecutive channels per lane
+// row-wise preparation: G = 2d/8 lanes per row, 8 consecutive channels per
+// lane (two 16-byte loads of each fp32 per-map output, one of dout), 64/G
+// rows per wave; row sums by shuffles within the G-lane group
 
 constexpr int kPrepThreads = 256;
+
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+  for (int off = G / 2; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
 
 template <int D>
 __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(BwdArgs a) {
   constexpr int DV = 2 * D;
-  constexpr int CPL = DV / 64;
+  constexpr int G = DV / 8;      // lanes per row
+  constexpr int RPW = 64 / G;    // rows per wave
   constexpr int WAVES = kPrepThreads / 64;
+  static_assert(G >= 8 && G <= 64 && 64 % G == 0, "row group");
   __shared__ float sdw[WAVES][DV];
   __shared__ float sdl[WAVES];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane / G, gl = lane % G;  // row within the wave, channel group
   const float lam = *a.lambda;
   const float sigma = a.out_scale;
   const long long rows = (long long)a.BH * a.N;
-  float w[CPL], dw[CPL];
+  float w[8], dw[8];
 #pragma unroll
-  for (int i = 0; i < CPL; ++i) {
-    w[i] = a.norm_w ? a.norm_w[lane * CPL + i] : 1.0f;
+  for (int i = 0; i < 8; ++i) {
+    w[i] = a.norm_w ? a.norm_w[8 * gl + i] : 1.0f;
     dw[i] = 0.f;
   }
   float dl = 0.f;
   const uint16_t* dout = (const uint16_t*)a.dout;
-  uint16_t* dy_out = a.dy;
-  for (long long row = (long long)blockIdx.x * WAVES + wave; row < rows; row += (long long)gridDim.x * WAVES) {
-    const float* o1 = a.osave + row * DV + lane * CPL;
-    const float* o2 = a.osave + (rows + row) * DV + lane * CPL;
-    const uint16_t* go = dout + row * DV + lane * CPL;
-    float y[CPL], g[CPL], x1[CPL], x2[CPL], gd[CPL];
+  const long long stride = (long long)gridDim.x * WAVES * RPW;
+  // the loop bound is wave-uniform: every lane takes part in the shuffles
+  for (long long base = ((long long)blockIdx.x * WAVES + wave) * RPW; base < rows; base += stride) {
+    const long long row = base + sub;
+    const bool valid = row < rows;
+    float x1[8], x2[8], gd[8], y[8];
+    if (valid) {
+      const f32x4* o1 = reinterpret_cast<const f32x4*>(a.osave + row * DV + 8 * gl);
+      const f32x4* o2 = reinterpret_cast<const f32x4*>(a.osave + (rows + row) * DV + 8 * gl);
+      const f32x4 p0 = o1[0], p1 = o1[1], r0 = o2[0], r1 = o2[1];
+      const u32x4 g = ld16(dout + row * DV + 8 * gl);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x1[i] = p0[i];
+        x1[4 + i] = p1[i];
+        x2[i] = r0[i];
+        x2[4 + i] = r1[i];
+        gd[2 * i] = bf16_lo(g[i]);
+        gd[2 * i + 1] = bf16_hi(g[i]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x1[i] = x2[i] = gd[i] = 0.f;
+    }
     float ss = 0.f;
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-      x1[i] = o1[i];
-      x2[i] = o2[i];
-      gd[i] = __builtin_bit_cast(float, (uint32_t)go[i] << 16);
+    for (int i = 0; i < 8; ++i) {
       y[i] = x1[i] - lam * x2[i];
       ss += y[i] * y[i];
     }
-    ss = wave_sum(ss);
+    ss = group_sum<G>(ss);
     const float ir = 1.0f / sqrtf(ss * (1.0f / DV) + a.eps);
     float gy = 0.f;
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-      g[i] = sigma * w[i] * gd[i];
-      gy += g[i] * y[i];
-    }
-    gy = wave_sum(gy);
+    for (int i = 0; i < 8; ++i) gy += sigma * w[i] * gd[i] * y[i];
+    gy = group_sum<G>(gy);
     const float k3 = gy * ir * ir * ir * (1.0f / DV);
     // delta_k is formed from dY as rounded to bf16, the dY the products
     // dP = dY V^T see, so that dP - delta cancels where it should (a row
     // with one visible key has dS = 0 exactly); dlambda uses the fp32 dY
     float t1 = 0.f, t2 = 0.f, u2 = 0.f;
-    uint16_t* dyp = dy_out + row * DV + lane * CPL;
+    uint32_t packed[4];
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-      const float dyv = g[i] * ir - y[i] * k3;
-      const uint16_t hb = (uint16_t)(pack_bf16x2(dyv, 0.f) & 0xffffu);
-      const float dyr = __builtin_bit_cast(float, (uint32_t)hb << 16);
-      t1 += dyr * x1[i];
-      t2 += dyr * x2[i];
-      u2 += dyv * x2[i];
-      dyp[i] = hb;
-      dw[i] += sigma * gd[i] * y[i] * ir;
+    for (int i = 0; i < 4; ++i) {
+      const float d0 = sigma * w[2 * i] * gd[2 * i] * ir - y[2 * i] * k3;
+      const float d1 = sigma * w[2 * i + 1] * gd[2 * i + 1] * ir - y[2 * i + 1] * k3;
+      packed[i] = pack_bf16x2(d0, d1);
+      const float r0 = bf16_lo(packed[i]), r1 = bf16_hi(packed[i]);
+      t1 += r0 * x1[2 * i] + r1 * x1[2 * i + 1];
+      t2 += r0 * x2[2 * i] + r1 * x2[2 * i + 1];
+      u2 += d0 * x2[2 * i] + d1 * x2[2 * i + 1];
     }
-    t1 = wave_sum(t1);
-    t2 = wave_sum(t2);
-    u2 = wave_sum(u2);
-    if (lane == 0) {
-      a.delta[row] = t1;
-      a.delta[rows + row] = -lam * t2;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dw[i] += sigma * gd[i] * y[i] * ir;
+    t1 = group_sum<G>(t1);
+    t2 = group_sum<G>(t2);
+    u2 = group_sum<G>(u2);
+    if (valid) {
+      const u32x4 pk = {packed[0], packed[1], packed[2], packed[3]};
+      st16(a.dy + row * DV + 8 * gl, pk);
+      if (gl == 0) {
+        a.delta[row] = t1;
+        a.delta[rows + row] = -lam * t2;
+        dl -= u2;
+      }
     }
-    dl -= u2;
   }
+  // this wave's sums over its rows: lanes of equal gl, then dlambda over the wave
 #pragma unroll
-  for (int i = 0; i < CPL; ++i) sdw[wave][lane * CPL + i] = dw[i];
+  for (int off = G; off < 64; off <<= 1)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dw[i] += __shfl_xor(dw[i], off);
+  dl = wave_sum(dl);
+  if (sub == 0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sdw[wave][8 * gl + i] = dw[i];
+  }
   if (lane == 0) sdl[wave] = dl;
   __syncthreads();
   float* part = a.partial + (size_t)blockIdx.x * (DV + 1);
@@ -379,6 +416,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 // wave and tile: S_k (32 queries x 16 keys) = Q_k K_k^T, dP = dY V^T, then
 //   dV^T += dY^T (A1 - lambda A2),  dK_k^T += Q_k^T dS_k.
 
+// One 16-key sub-tile per wave: with two (each Q / dY fragment read feeding
+// two products, as in the dQ kernel) the dK1, dK2 and dV accumulators alone
+// take 128 registers at d = 64 and the kernel needs 416 (one wave per SIMD);
+// that measured 19% slower than this form (66% slower squeezed into 256
+// registers with spills).
 constexpr int kDkvKeys = 64;
 constexpr int kDkvRows = 32;
 
