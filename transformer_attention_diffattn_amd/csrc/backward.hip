@@ -70,6 +70,14 @@ __device__ __forceinline__ void dma_block(const uint16_t* src, int C, int cb, in
   lds_dma16_s(src, (uint32_t)(r * C + 16 * cb + 8 * (lane & 1)) * 2u, lds_block);
 }
 
+// Make the compiler wait for a register's pending load here, where nothing
+// else is in flight: inside a loop it cannot see the asynchronous tile
+// loads and would wait for them too.
+template <typename T>
+__device__ __forceinline__ void settle(T& x) {
+  asm volatile("" : "+v"(x));
+}
+
 // A operand with k over 32 rows starting at r0 of column block cb (R-row tile)
 template <int R>
 __device__ __forceinline__ bf16x8 tr_frag(const uint16_t* tile, int cb, int r0, int lane) {
@@ -302,6 +310,21 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     dl2[u] = a.delta[nrows + hb + qc];
   }
 
+#pragma unroll
+  for (int u = 0; u < SUB; ++u) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      settle(qf1[u][ks]);
+      settle(qf2[u][ks]);
+    }
+#pragma unroll
+    for (int kv = 0; kv < KV; ++kv) settle(dyf[u][kv]);
+    settle(lse1[u]);
+    settle(lse2[u]);
+    settle(dl1[u]);
+    settle(dl2[u]);
+  }
+
   f32x4 dq1[SUB][DB], dq2[SUB][DB];
 #pragma unroll
   for (int u = 0; u < SUB; ++u)
@@ -425,7 +448,7 @@ constexpr int kDkvKeys = 64;
 constexpr int kDkvRows = 32;
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdArgs a) {
   constexpr int DV = 2 * D, KS = D / 32, KV = DV / 32, DB = D / 16, CB = DV / 16, BQ = kDkvRows;
   static_assert(BQ == kTileRows, "one load instruction per 32-row column block");
   constexpr int STAGE = 2 * BQ * D + BQ * DV;  // Q1, Q2, dY tiles
@@ -457,6 +480,14 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdArgs a) {
   }
 #pragma unroll
   for (int kv = 0; kv < KV; ++kv) vf[kv] = as_bf16x8(ld16(V + (size_t)kc * DV + 32 * kv + 8 * lg));
+
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    settle(kf1[ks]);
+    settle(kf2[ks]);
+  }
+#pragma unroll
+  for (int kv = 0; kv < KV; ++kv) settle(vf[kv]);
 
   f32x4 dk1[DB], dk2[DB], dv[CB];
 #pragma unroll
