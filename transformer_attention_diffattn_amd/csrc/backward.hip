@@ -62,7 +62,15 @@ __device__ __forceinline__ float wave_sum(float x) {
 // 16 cb + 8 (L % 2) .. + 7, which the blocked layout puts at byte 16 L of
 // the block -- the position the instruction writes lane L's 16 bytes to.
 constexpr int kTileRows = 32;
-constexpr int kStages = 3;
+// Stage buffers: three (two tiles loading ahead) where two workgroups still
+// fit a compute unit's LDS.  For the dQ kernel at d = 128 three would take
+// 96 KB and leave one workgroup per CU, whose accumulators the compiler then
+// shuttles through AGPRs, so two; the dK/dV kernel at d = 128 needs more
+// than 256 registers and runs one wave per SIMD anyway, so it keeps three.
+template <int D, bool DQ>
+struct BwdStages {
+  static constexpr int N = (DQ && D >= 128) ? 2 : 3;
+};
 
 __device__ __forceinline__ void dma_block(const uint16_t* src, int C, int cb, int r0, int n_rows, int lane,
                                           uint32_t lds_block) {
@@ -269,6 +277,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   static_assert(BN == kTileRows, "one load instruction per 32-row column block");
   constexpr int STAGE = 2 * BN * D + BN * DV;  // K1, K2, V tiles
   constexpr int NI = D / 16;                   // load instructions per wave and tile
+  constexpr int kStages = BwdStages<D, true>::N;
   __shared__ __attribute__((aligned(16))) uint16_t stg[kStages * STAGE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
@@ -352,17 +361,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     }
   };
   issue(0);
-  if (nkt > 1) issue(1);
+  if (kStages == 3 && nkt > 1) issue(1);
   for (int kt = 0; kt < nkt; ++kt) {
     const int k0 = kt * BN;
-    // tile kt has landed (only tile kt+1 may still load) for every wave, and
-    // everybody is done with tile kt-1, whose buffer tile kt+2 reuses
-    if (kt + 1 < nkt)
+    // tile kt has landed (with three stages tile kt+1 may still load) for
+    // every wave, and everybody is done with the buffer the next issue reuses
+    if (kStages == 3 && kt + 1 < nkt)
       wait_vmem_keep<NI>();
     else
       wait_vmem();
     __syncthreads();
-    if (kt + 2 < nkt) issue(kt + 2);
+    if (kt + kStages - 1 < nkt) issue(kt + kStages - 1);
     const uint16_t* sk1 = stg + (kt % kStages) * STAGE;
     const uint16_t* sk2 = sk1 + BN * D;
     const uint16_t* sv = sk1 + 2 * BN * D;
@@ -401,6 +410,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
           g1[u][kb][j] = e1 * (dp[u][j] - dl1[u]);
           g2[u][kb][j] = e2 * (-lam * dp[u][j] - dl2[u]);
         }
+      // at d = 128, keep the next block's fragment reads from being hoisted
+      // here: all of a tile's fragments live at once would not fit
+      if (D >= 128) __builtin_amdgcn_sched_barrier(0);
     }
     bf16x8 b1[SUB], b2[SUB];
 #pragma unroll
@@ -448,11 +460,12 @@ constexpr int kDkvKeys = 64;
 constexpr int kDkvRows = 32;
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, D >= 128 ? 1 : 2) void bwd_dkv_kernel(BwdArgs a) {
   constexpr int DV = 2 * D, KS = D / 32, KV = DV / 32, DB = D / 16, CB = DV / 16, BQ = kDkvRows;
   static_assert(BQ == kTileRows, "one load instruction per 32-row column block");
   constexpr int STAGE = 2 * BQ * D + BQ * DV;  // Q1, Q2, dY tiles
   constexpr int NI = D / 16;                   // tile load instructions per wave and tile
+  constexpr int kStages = BwdStages<D, false>::N;
   __shared__ __attribute__((aligned(16))) uint16_t stg[kStages * STAGE];
   __shared__ __attribute__((aligned(16))) float sstat[kStages][4][BQ];  // lse1, lse2, delta1, delta2
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -528,12 +541,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdArgs a) {
     }
   };
   issue(qt0);
-  if (qt0 + 1 < nqt) issue(qt0 + 1);
+  if (kStages == 3 && qt0 + 1 < nqt) issue(qt0 + 1);
   for (int qt = qt0; qt < nqt; ++qt) {
     const int q0 = qt * BQ;
-    // tile qt has landed (only tile qt+1 may still load) for every wave, and
-    // everybody is done with tile qt-1, whose buffer tile qt+2 reuses
-    if (qt + 1 < nqt) {
+    // tile qt has landed (with three stages tile qt+1 may still load) for
+    // every wave, and everybody is done with the buffer the next issue reuses
+    if (kStages == 3 && qt + 1 < nqt) {
       if (wave < 2)
         wait_vmem_keep<NI + 1>();
       else
@@ -542,7 +555,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdArgs a) {
       wait_vmem();
     }
     __syncthreads();
-    if (qt + 2 < nqt) issue(qt + 2);
+    if (qt + kStages - 1 < nqt) issue(qt + kStages - 1);
     const uint16_t* sq1 = stg + (qt % kStages) * STAGE;
     const uint16_t* sq2 = sq1 + BQ * D;
     const uint16_t* sdy = sq1 + 2 * BQ * D;
@@ -575,6 +588,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdArgs a) {
         gs1[qb][j] = e1 * (dp[j] - t1[j]);
         gs2[qb][j] = e2 * (-lam * dp[j] - t2[j]);
       }
+      if (D >= 128) __builtin_amdgcn_sched_barrier(0);  // as in the dQ kernel
     }
     const bf16x8 bd = pack_frag(d1), b1 = pack_frag(gs1), b2 = pack_frag(gs2);
 #pragma unroll
