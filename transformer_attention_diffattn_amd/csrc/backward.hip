@@ -35,6 +35,8 @@
 // rounded to bf16 in-lane, are the B operand of a product whose k runs over
 // those rows, in the same row order as the transposing read delivers them.
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -279,7 +281,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   constexpr int NI = D / 16;                   // load instructions per wave and tile
   constexpr int kStages = BwdStages<D, true>::N;
   __shared__ __attribute__((aligned(16))) uint16_t stg[kStages * STAGE];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: branches on it stay uniform
   const int lr = lane & 15, lg = lane >> 4;
   const int N = a.N, BH = a.BH;
   const int nqt = (N + ROWS - 1) / ROWS;
@@ -378,42 +381,53 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     if (qw >= N || (CAUSAL && k0 > qw + 16 * SUB - 1)) continue;  // nothing visible to this wave
 
     float g1[SUB][2][4], g2[SUB][2][4];
+    // the tile holds keys past a row of this wave's diagonal, or keys or
+    // rows past N: only such tiles pay for the per-element mask
+    const bool masked = (CAUSAL && k0 + BN - 1 > qw) || k0 + BN > N || qw + 16 * SUB > N;
+    auto scores = [&](auto mask_tag) {
+      constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x4 s1[SUB], s2[SUB], dp[SUB];
+      for (int kb = 0; kb < 2; ++kb) {
+        f32x4 s1[SUB], s2[SUB], dp[SUB];
 #pragma unroll
-      for (int u = 0; u < SUB; ++u) s1[u] = s2[u] = dp[u] = zero_f32x4();
+        for (int u = 0; u < SUB; ++u) s1[u] = s2[u] = dp[u] = zero_f32x4();
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 a1 = as_bf16x8(ld16(sk1 + boff<BN>(16 * kb + lr, 32 * ks + 8 * lg)));
-        const bf16x8 a2 = as_bf16x8(ld16(sk2 + boff<BN>(16 * kb + lr, 32 * ks + 8 * lg)));
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 a1 = as_bf16x8(ld16(sk1 + boff<BN>(16 * kb + lr, 32 * ks + 8 * lg)));
+          const bf16x8 a2 = as_bf16x8(ld16(sk2 + boff<BN>(16 * kb + lr, 32 * ks + 8 * lg)));
 #pragma unroll
-        for (int u = 0; u < SUB; ++u) {
-          s1[u] = mfma16x16x32_bf16(a1, qf1[u][ks], s1[u]);
-          s2[u] = mfma16x16x32_bf16(a2, qf2[u][ks], s2[u]);
+          for (int u = 0; u < SUB; ++u) {
+            s1[u] = mfma16x16x32_bf16(a1, qf1[u][ks], s1[u]);
+            s2[u] = mfma16x16x32_bf16(a2, qf2[u][ks], s2[u]);
+          }
         }
-      }
 #pragma unroll
-      for (int kv = 0; kv < KV; ++kv) {
-        const bf16x8 av = as_bf16x8(ld16(sv + boff<BN>(16 * kb + lr, 32 * kv + 8 * lg)));
+        for (int kv = 0; kv < KV; ++kv) {
+          const bf16x8 av = as_bf16x8(ld16(sv + boff<BN>(16 * kb + lr, 32 * kv + 8 * lg)));
 #pragma unroll
-        for (int u = 0; u < SUB; ++u) dp[u] = mfma16x16x32_bf16(av, dyf[u][kv], dp[u]);
-      }
-#pragma unroll
-      for (int u = 0; u < SUB; ++u)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int key = k0 + 16 * kb + 4 * lg + j;
-          const bool ok = key < N && q[u] < N && (!CAUSAL || key <= q[u]);
-          const float e1 = ok ? exp2_fast(s1[u][j] * c - lse1[u]) : 0.f;
-          const float e2 = ok ? exp2_fast(s2[u][j] * c - lse2[u]) : 0.f;
-          g1[u][kb][j] = e1 * (dp[u][j] - dl1[u]);
-          g2[u][kb][j] = e2 * (-lam * dp[u][j] - dl2[u]);
+          for (int u = 0; u < SUB; ++u) dp[u] = mfma16x16x32_bf16(av, dyf[u][kv], dp[u]);
         }
-      // at d = 128, keep the next block's fragment reads from being hoisted
-      // here: all of a tile's fragments live at once would not fit
-      if (D >= 128) __builtin_amdgcn_sched_barrier(0);
-    }
+#pragma unroll
+        for (int u = 0; u < SUB; ++u)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int key = k0 + 16 * kb + 4 * lg + j;
+            const bool ok = !MASK || (key < N && q[u] < N && (!CAUSAL || key <= q[u]));
+            const float e1 = ok ? exp2_fast(s1[u][j] * c - lse1[u]) : 0.f;
+            const float e2 = ok ? exp2_fast(s2[u][j] * c - lse2[u]) : 0.f;
+            g1[u][kb][j] = e1 * (dp[u][j] - dl1[u]);
+            g2[u][kb][j] = e2 * (-lam * dp[u][j] - dl2[u]);
+          }
+        // at d = 128, keep the next block's fragment reads from being hoisted
+        // here: all of a tile's fragments live at once would not fit
+        if (D >= 128) __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    // (at d = 128 a second copy of the tile body would not fit the registers)
+    if (D >= 128 || masked)
+      scores(std::true_type{});
+    else
+      scores(std::false_type{});
     bf16x8 b1[SUB], b2[SUB];
 #pragma unroll
     for (int u = 0; u < SUB; ++u) {
@@ -468,7 +482,8 @@ __global__ __launch_bounds__(256, D >= 128 ? 1 : 2) void bwd_dkv_kernel(BwdArgs 
   constexpr int kStages = BwdStages<D, false>::N;
   __shared__ __attribute__((aligned(16))) uint16_t stg[kStages * STAGE];
   __shared__ __attribute__((aligned(16))) float sstat[kStages][4][BQ];  // lse1, lse2, delta1, delta2
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: branches on it stay uniform
   const int lr = lane & 15, lg = lane >> 4;
   const int N = a.N, BH = a.BH;
   const int bh = blockIdx.x % BH;
@@ -563,33 +578,43 @@ __global__ __launch_bounds__(256, D >= 128 ? 1 : 2) void bwd_dkv_kernel(BwdArgs 
     if (kw >= N || (CAUSAL && q0 + BQ - 1 < kw)) continue;  // nothing visible to this wave
 
     float d1[2][4], gs1[2][4], gs2[2][4];
+    // the tile holds rows before one of this wave's keys, or rows or keys
+    // past N: only such tiles pay for the per-element mask
+    const bool masked = (CAUSAL && q0 < kw + 15) || q0 + BQ > N || kw + 16 > N;
+    auto scores = [&](auto mask_tag) {
+      constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      f32x4 s1 = zero_f32x4(), s2 = zero_f32x4(), dp = zero_f32x4();
+      for (int qb = 0; qb < 2; ++qb) {
+        f32x4 s1 = zero_f32x4(), s2 = zero_f32x4(), dp = zero_f32x4();
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        s1 = mfma16x16x32_bf16(as_bf16x8(ld16(sq1 + boff<BQ>(16 * qb + lr, 32 * ks + 8 * lg))), kf1[ks], s1);
-        s2 = mfma16x16x32_bf16(as_bf16x8(ld16(sq2 + boff<BQ>(16 * qb + lr, 32 * ks + 8 * lg))), kf2[ks], s2);
+        for (int ks = 0; ks < KS; ++ks) {
+          s1 = mfma16x16x32_bf16(as_bf16x8(ld16(sq1 + boff<BQ>(16 * qb + lr, 32 * ks + 8 * lg))), kf1[ks], s1);
+          s2 = mfma16x16x32_bf16(as_bf16x8(ld16(sq2 + boff<BQ>(16 * qb + lr, 32 * ks + 8 * lg))), kf2[ks], s2);
+        }
+#pragma unroll
+        for (int kv = 0; kv < KV; ++kv)
+          dp = mfma16x16x32_bf16(as_bf16x8(ld16(sdy + boff<BQ>(16 * qb + lr, 32 * kv + 8 * lg))), vf[kv], dp);
+        const f32x4 l1 = *reinterpret_cast<const f32x4*>(&sst[0][16 * qb + 4 * lg]);
+        const f32x4 l2 = *reinterpret_cast<const f32x4*>(&sst[1][16 * qb + 4 * lg]);
+        const f32x4 t1 = *reinterpret_cast<const f32x4*>(&sst[2][16 * qb + 4 * lg]);
+        const f32x4 t2 = *reinterpret_cast<const f32x4*>(&sst[3][16 * qb + 4 * lg]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int qi = q0 + 16 * qb + 4 * lg + j;
+          const bool ok = !MASK || (qi < N && kk < N && (!CAUSAL || kk <= qi));
+          const float e1 = ok ? exp2_fast(s1[j] * c - l1[j]) : 0.f;
+          const float e2 = ok ? exp2_fast(s2[j] * c - l2[j]) : 0.f;
+          d1[qb][j] = e1 - lam * e2;
+          gs1[qb][j] = e1 * (dp[j] - t1[j]);
+          gs2[qb][j] = e2 * (-lam * dp[j] - t2[j]);
+        }
+        if (D >= 128) __builtin_amdgcn_sched_barrier(0);  // as in the dQ kernel
       }
-#pragma unroll
-      for (int kv = 0; kv < KV; ++kv)
-        dp = mfma16x16x32_bf16(as_bf16x8(ld16(sdy + boff<BQ>(16 * qb + lr, 32 * kv + 8 * lg))), vf[kv], dp);
-      const f32x4 l1 = *reinterpret_cast<const f32x4*>(&sst[0][16 * qb + 4 * lg]);
-      const f32x4 l2 = *reinterpret_cast<const f32x4*>(&sst[1][16 * qb + 4 * lg]);
-      const f32x4 t1 = *reinterpret_cast<const f32x4*>(&sst[2][16 * qb + 4 * lg]);
-      const f32x4 t2 = *reinterpret_cast<const f32x4*>(&sst[3][16 * qb + 4 * lg]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int qi = q0 + 16 * qb + 4 * lg + j;
-        const bool ok = qi < N && kk < N && (!CAUSAL || kk <= qi);
-        const float e1 = ok ? exp2_fast(s1[j] * c - l1[j]) : 0.f;
-        const float e2 = ok ? exp2_fast(s2[j] * c - l2[j]) : 0.f;
-        d1[qb][j] = e1 - lam * e2;
-        gs1[qb][j] = e1 * (dp[j] - t1[j]);
-        gs2[qb][j] = e2 * (-lam * dp[j] - t2[j]);
-      }
-      if (D >= 128) __builtin_amdgcn_sched_barrier(0);  // as in the dQ kernel
-    }
+    };
+    if (masked)
+      scores(std::true_type{});
+    else
+      scores(std::false_type{});
     const bf16x8 bd = pack_frag(d1), b1 = pack_frag(gs1), b2 = pack_frag(gs2);
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) dv[cb] = mfma16x16x32_bf16(tr_frag<BQ>(sdy, cb, 0, lane), bd, dv[cb]);
