@@ -65,13 +65,12 @@ __device__ __forceinline__ float wave_sum(float x) {
 // the block -- the position the instruction writes lane L's 16 bytes to.
 constexpr int kTileRows = 32;
 // Stage buffers: three (two tiles loading ahead) where two workgroups still
-// fit a compute unit's LDS.  For the dQ kernel at d = 128 three would take
-// 96 KB and leave one workgroup per CU, whose accumulators the compiler then
-// shuttles through AGPRs, so two; the dK/dV kernel at d = 128 needs more
-// than 256 registers and runs one wave per SIMD anyway, so it keeps three.
+// fit a compute unit's LDS.  At d = 128 three would take 96 KB and leave one
+// workgroup per CU, whose accumulators the compiler then shuttles through
+// AGPRs, so two.
 template <int D, bool DQ>
 struct BwdStages {
-  static constexpr int N = (DQ && D >= 128) ? 2 : 3;
+  static constexpr int N = D >= 128 ? 2 : 3;
 };
 
 __device__ __forceinline__ void dma_block(const uint16_t* src, int C, int cb, int r0, int n_rows, int lane,
@@ -470,11 +469,18 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 // take 128 registers at d = 64 and the kernel needs 416 (one wave per SIMD);
 // that measured 19% slower than this form (66% slower squeezed into 256
 // registers with spills).
+// At d = 128 one kernel holding dK1, dK2 and dV (128 accumulator registers)
+// plus the K and V operands needs more than 256 registers (one wave per SIMD,
+// accumulators shuttled through AGPRs), so there the work is split over two
+// launches of this kernel: MODE 1 accumulates dV only, MODE 2 dK1 and dK2
+// only; each evaluates S again (20 d instead of 16 d flops per pair) but
+// runs two waves per SIMD.  MODE 0 does both (d <= 64).
 constexpr int kDkvKeys = 64;
 constexpr int kDkvRows = 32;
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, D >= 128 ? 1 : 2) void bwd_dkv_kernel(BwdArgs a) {
+template <int D, bool CAUSAL, int MODE>
+__global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdArgs a) {
+  constexpr bool DO_DV = MODE != 2, DO_DK = MODE != 1;
   constexpr int DV = 2 * D, KS = D / 32, KV = DV / 32, DB = D / 16, CB = DV / 16, BQ = kDkvRows;
   static_assert(BQ == kTileRows, "one load instruction per 32-row column block");
   constexpr int STAGE = 2 * BQ * D + BQ * DV;  // Q1, Q2, dY tiles
@@ -506,16 +512,20 @@ __global__ __launch_bounds__(256, D >= 128 ? 1 : 2) void bwd_dkv_kernel(BwdArgs 
     kf1[ks] = as_bf16x8(ld16(K1 + (size_t)kc * D + 32 * ks + 8 * lg));
     kf2[ks] = as_bf16x8(ld16(K2 + (size_t)kc * D + 32 * ks + 8 * lg));
   }
+  if constexpr (DO_DK) {
 #pragma unroll
-  for (int kv = 0; kv < KV; ++kv) vf[kv] = as_bf16x8(ld16(V + (size_t)kc * DV + 32 * kv + 8 * lg));
+    for (int kv = 0; kv < KV; ++kv) vf[kv] = as_bf16x8(ld16(V + (size_t)kc * DV + 32 * kv + 8 * lg));
+  }
 
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     settle(kf1[ks]);
     settle(kf2[ks]);
   }
+  if constexpr (DO_DK) {
 #pragma unroll
-  for (int kv = 0; kv < KV; ++kv) settle(vf[kv]);
+    for (int kv = 0; kv < KV; ++kv) settle(vf[kv]);
+  }
 
   f32x4 dk1[DB], dk2[DB], dv[CB];
 #pragma unroll
@@ -591,9 +601,11 @@ __global__ __launch_bounds__(256, D >= 128 ? 1 : 2) void bwd_dkv_kernel(BwdArgs 
           s1 = mfma16x16x32_bf16(as_bf16x8(ld16(sq1 + boff<BQ>(16 * qb + lr, 32 * ks + 8 * lg))), kf1[ks], s1);
           s2 = mfma16x16x32_bf16(as_bf16x8(ld16(sq2 + boff<BQ>(16 * qb + lr, 32 * ks + 8 * lg))), kf2[ks], s2);
         }
+        if constexpr (DO_DK) {
 #pragma unroll
-        for (int kv = 0; kv < KV; ++kv)
-          dp = mfma16x16x32_bf16(as_bf16x8(ld16(sdy + boff<BQ>(16 * qb + lr, 32 * kv + 8 * lg))), vf[kv], dp);
+          for (int kv = 0; kv < KV; ++kv)
+            dp = mfma16x16x32_bf16(as_bf16x8(ld16(sdy + boff<BQ>(16 * qb + lr, 32 * kv + 8 * lg))), vf[kv], dp);
+        }
         const f32x4 l1 = *reinterpret_cast<const f32x4*>(&sst[0][16 * qb + 4 * lg]);
         const f32x4 l2 = *reinterpret_cast<const f32x4*>(&sst[1][16 * qb + 4 * lg]);
         const f32x4 t1 = *reinterpret_cast<const f32x4*>(&sst[2][16 * qb + 4 * lg]);
@@ -615,27 +627,36 @@ __global__ __launch_bounds__(256, D >= 128 ? 1 : 2) void bwd_dkv_kernel(BwdArgs 
       scores(std::true_type{});
     else
       scores(std::false_type{});
-    const bf16x8 bd = pack_frag(d1), b1 = pack_frag(gs1), b2 = pack_frag(gs2);
+    if constexpr (DO_DV) {
+      const bf16x8 bd = pack_frag(d1);
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) dv[cb] = mfma16x16x32_bf16(tr_frag<BQ>(sdy, cb, 0, lane), bd, dv[cb]);
+      for (int cb = 0; cb < CB; ++cb) dv[cb] = mfma16x16x32_bf16(tr_frag<BQ>(sdy, cb, 0, lane), bd, dv[cb]);
+    }
+    if constexpr (DO_DK) {
+      const bf16x8 b1 = pack_frag(gs1), b2 = pack_frag(gs2);
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      dk1[db] = mfma16x16x32_bf16(tr_frag<BQ>(sq1, db, 0, lane), b1, dk1[db]);
-      dk2[db] = mfma16x16x32_bf16(tr_frag<BQ>(sq2, db, 0, lane), b2, dk2[db]);
+      for (int db = 0; db < DB; ++db) {
+        dk1[db] = mfma16x16x32_bf16(tr_frag<BQ>(sq1, db, 0, lane), b1, dk1[db]);
+        dk2[db] = mfma16x16x32_bf16(tr_frag<BQ>(sq2, db, 0, lane), b2, dk2[db]);
+      }
     }
   }
   if (kk < N) {
     const float s = 1.0f / sqrtf((float)D);
-    uint16_t* o1 = (uint16_t*)a.dk1 + (hb + kk) * D;
-    uint16_t* o2 = (uint16_t*)a.dk2 + (hb + kk) * D;
-    uint16_t* ov = (uint16_t*)a.dv + (hb + kk) * DV;
+    if constexpr (DO_DK) {
+      uint16_t* o1 = (uint16_t*)a.dk1 + (hb + kk) * D;
+      uint16_t* o2 = (uint16_t*)a.dk2 + (hb + kk) * D;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      store_bf16x4(o1 + 16 * db + 4 * lg, dk1[db], s);
-      store_bf16x4(o2 + 16 * db + 4 * lg, dk2[db], s);
+      for (int db = 0; db < DB; ++db) {
+        store_bf16x4(o1 + 16 * db + 4 * lg, dk1[db], s);
+        store_bf16x4(o2 + 16 * db + 4 * lg, dk2[db], s);
+      }
     }
+    if constexpr (DO_DV) {
+      uint16_t* ov = (uint16_t*)a.dv + (hb + kk) * DV;
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) store_bf16x4(ov + 16 * cb + 4 * lg, dv[cb], 1.0f);
+      for (int cb = 0; cb < CB; ++cb) store_bf16x4(ov + 16 * cb + 4 * lg, dv[cb], 1.0f);
+    }
   }
 }
 
@@ -681,7 +702,12 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
   const unsigned gq = (unsigned)(((a.N + DqCfg<D>::ROWS - 1) / DqCfg<D>::ROWS) * (long long)a.BH);
   hipLaunchKernelGGL((bwd_dq_kernel<D, C>), dim3(gq), dim3(256), 0, s, a);
   const unsigned gk = (unsigned)(((a.N + kDkvKeys - 1) / kDkvKeys) * (long long)a.BH);
-  hipLaunchKernelGGL((bwd_dkv_kernel<D, C>), dim3(gk), dim3(256), 0, s, a);
+  if constexpr (D >= 128) {
+    hipLaunchKernelGGL((bwd_dkv_kernel<D, C, 1>), dim3(gk), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((bwd_dkv_kernel<D, C, 2>), dim3(gk), dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((bwd_dkv_kernel<D, C, 0>), dim3(gk), dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 
