@@ -173,7 +173,8 @@ def backward_leg(x, w, args, stream, torch, da):
     from a HIP graph (checked equal to the eager call).  The backward is priced
     at its algorithmic 20 d flops per causal pair (two QK^T products 4 d, dP 4 d,
     dV 4 d, dK1 + dK2 4 d, dQ1 + dQ2 4 d); the kernels execute 28 d, because
-    the query-parallel dQ kernel evaluates S and dP again."""
+    the query-parallel dQ kernel evaluates S and dP again (32 d at d = 128,
+where dV and dK are also computed apart)."""
     dev = x["q1"].device
     gen = torch.Generator(device=dev)
     gen.manual_seed(w.seed + 7)

@@ -17,13 +17,14 @@
 //
 // The forward run in training mode keeps, per map and row, the log2-sum-exp
 // of the scaled scores and O_k; A_k is recomputed here as
-// 2^(s log2(e)/sqrt(d) - lse_k).  Four launches:
+// 2^(s log2(e)/sqrt(d) - lse_k).  The launches:
 //   bwd_prep_kernel    row-wise: Y, r, dY (bf16), delta1, delta2, and per-
 //                      workgroup partial sums of dw and dlambda;
+//   bwd_reduce_kernel  the partial sums in a fixed order (deterministic);
 //   bwd_dq_kernel      query-parallel: S^T, dP^T and dQ^T += K^T dS^T;
 //   bwd_dkv_kernel     key-parallel: S, dP and dV^T += dY^T D,
-//                      dK^T += Q^T dS (D = A1 - lambda A2);
-//   bwd_reduce_kernel  the partial sums in a fixed order (deterministic).
+//                      dK^T += Q^T dS (D = A1 - lambda A2); at d = 128 as
+//                      two launches, dV and dK apart (registers).
 // Splitting dQ from dK/dV costs a second evaluation of S and dP but needs no
 // atomics, so every gradient is deterministic.
 //
