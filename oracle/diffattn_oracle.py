@@ -63,6 +63,7 @@ __all__ = [
     "decode",
     "map_stats",
     "backward",
+    "backward_dq_rows",
 ]
 
 
@@ -290,3 +291,39 @@ def backward(q1, k1, q2, k2, v, lq1, lk1, lq2, lk2, lambda_init: float, dout,
                  dlq1=dlam * e1 * lk1, dlk1=dlam * e1 * lq1,
                  dlq2=-dlam * e2 * lk2, dlk2=-dlam * e2 * lq2)
     return grads
+
+
+def backward_dq_rows(q1, k1, q2, k2, v, rows, lq1, lk1, lq2, lk2, lambda_init: float, dout_rows,
+                     weight=None, eps: float = 1e-5, causal: bool = True):
+    """dQ1 and dQ2 of the given query rows only, for one head.
+
+    q1, k1, q2, k2: [N, d]; v: [N, 2d]; rows: 1-D ints; dout_rows: [len(rows), 2d],
+    the output gradient of those rows.  The same chain rule as ``backward``,
+    taken one row at a time: a row's dQ needs only that row's Y (its own
+    forward row), its dY, and its scores against the keys it sees, so each
+    row costs O(N d) and long sequences can be checked on sampled rows.
+    Returns (dq1 [len(rows), d], dq2 [len(rows), d]).
+    """
+    q1, k1, q2, k2, v, g_out = (_f64(t) for t in (q1, k1, q2, k2, v, dout_rows))
+    lam = lambda_scalar(lq1, lk1, lq2, lk2, lambda_init)
+    sigma = 1.0 - float(lambda_init)
+    d = q1.shape[-1]
+    n = v.shape[-1]
+    w = np.ones(n) if weight is None else _f64(weight)
+    rows = np.asarray(rows)
+    dq1 = np.zeros((len(rows), d))
+    dq2 = np.zeros((len(rows), d))
+    for r_i, i in enumerate(rows):
+        kmax = int(i) + 1 if causal else k1.shape[0]
+        a1 = softmax_rows((k1[:kmax] @ q1[i]) / math.sqrt(d))
+        a2 = softmax_rows((k2[:kmax] @ q2[i]) / math.sqrt(d))
+        y = (a1 - lam * a2) @ v[:kmax]
+        r = math.sqrt(float(np.mean(y * y)) + float(eps))
+        g = sigma * w * g_out[r_i]
+        dy = g / r - y * float(np.dot(g, y)) / (n * r ** 3)
+        da = v[:kmax] @ dy  # dL/dA1 for this row's keys; dL/dA2 = -lam * da
+        ds1 = a1 * (da - float(np.dot(a1, da)))
+        ds2 = a2 * (-lam * da - float(np.dot(a2, -lam * da)))
+        dq1[r_i] = ds1 @ k1[:kmax] / math.sqrt(d)
+        dq2[r_i] = ds2 @ k2[:kmax] / math.sqrt(d)
+    return dq1, dq2

@@ -28,6 +28,9 @@ REL = 2e-2
 # the row sum behind the saved log2-sum-exp adds bf16-rounded weights (each
 # within a relative 2^-9), so |d log2 L| <= 2^-9 / ln 2 = 2.8e-3
 LSE_TOL = 3e-3
+# sum over keys of dK: rounding each dK to bf16 moves the sum by at most
+# 2^-9 of sum |dK|; twice that leaves room for the bf16 rounding of dS
+KEY_SUM_TOL = 4e-3
 
 
 @pytest.fixture(scope="module")
@@ -166,3 +169,37 @@ def test_full_size_backward_sampled_heads(dev, name):
                          causal=True)
         got = {k: gr[k][b, h].float().cpu().numpy() for k in ("dq1", "dk1", "dq2", "dk2", "dv")}
         _compare(got, {k: ref[k][0, 0] for k in got}, tuple(got))
+
+
+def test_longctx_backward_sampled_rows_and_key_sums(dev):
+    """The 64K-token workload (needles included) in one launch.  The dense
+    oracle backward does not fit this length, so: dQ1 and dQ2 on sampled rows
+    (needle offsets, first and last rows) from the row-wise oracle, and for
+    every head the property that each map's dK sums to zero over the keys
+    (every row of dS sums to zero), to KEY_SUM_TOL of the sum of |dK|."""
+    name = "longctx_bf16_b1h12n65536d128"
+    print(f"case bwd full {name}", flush=True)
+    w = W.WORKLOADS[name]
+    x = W.workload_inputs(name)
+    gen = torch.Generator().manual_seed(w.seed + 7)
+    x["dout"] = torch.randn(x["v"].shape, generator=gen).to(torch.bfloat16)
+    g = {k: (t.to(dev) if torch.is_tensor(t) else t) for k, t in x.items()}
+    lam_t = da.lam(g["lq1"], g["lk1"], g["lq2"], g["lk2"], g["lambda_init"])
+    _, lse, o12 = da.fwd_train(g["q1"], g["k1"], g["q2"], g["k2"], g["v"], lam_t, g["lambda_init"], eps=g["eps"])
+    gr = da.bwd(g["q1"], g["k1"], g["q2"], g["k2"], g["v"], g["dout"], lse, o12, lam_t, g["lambda_init"],
+                eps=g["eps"])
+    torch.cuda.synchronize()
+    rows = np.array([0, 6, 7, 311, 5003, 40009, 65534, 65535])
+    for h in (0, w.H - 1):
+        sl = lambda t: t[0, h]
+        d1, d2 = O.backward_dq_rows(sl(x["q1"]), sl(x["k1"]), sl(x["q2"]), sl(x["k2"]), sl(x["v"]), rows,
+                                    x["lq1"], x["lk1"], x["lq2"], x["lk2"], x["lambda_init"],
+                                    sl(x["dout"])[rows], eps=x["eps"])
+        got = {"dq1": gr["dq1"][0, h][rows].float().cpu().numpy(), "dq2": gr["dq2"][0, h][rows].float().cpu().numpy()}
+        _compare(got, {"dq1": d1, "dq2": d2, "dv": np.zeros(1)}, ("dq1", "dq2"))
+    for k in ("dk1", "dk2"):
+        t = gr[k][0].float()  # [H, N, d]
+        s = t.sum(dim=1).abs().max().item()
+        a = t.abs().sum(dim=1).max().item()
+        print(f"{k}: max |sum_j dK| = {s:.3e}, max sum_j |dK| = {a:.3e}", flush=True)
+        assert s <= KEY_SUM_TOL * a, (k, s, a)

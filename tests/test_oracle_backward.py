@@ -111,3 +111,28 @@ def test_map_stats_match_library_routines():
     lam = 0.37
     y = O.pre_norm(q1, k1, q2, k2, v, lam, causal=True)
     assert np.max(np.abs((o1 - lam * o2) - y)) < 1e-12
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_backward_dq_rows_match_backward(causal):
+    """The row-at-a-time dQ equals the full backward's dQ rows."""
+    x = _case(23, 1, 1, 41, 8)
+    g = O.backward(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], x["lq1"], x["lk1"], x["lq2"], x["lk2"],
+                   x["lambda_init"], x["dout"], weight=x["weight"], eps=1e-5, causal=causal)
+    rows = np.array([0, 1, 17, 40])
+    sl = lambda k: x[k][0, 0]
+    d1, d2 = O.backward_dq_rows(sl("q1"), sl("k1"), sl("q2"), sl("k2"), sl("v"), rows, x["lq1"], x["lk1"],
+                                x["lq2"], x["lk2"], x["lambda_init"], x["dout"][0, 0][rows], weight=x["weight"],
+                                eps=1e-5, causal=causal)
+    assert np.max(np.abs(d1 - g["dq1"][0, 0][rows])) < 1e-12
+    assert np.max(np.abs(d2 - g["dq2"][0, 0][rows])) < 1e-12
+
+
+def test_backward_dk_sums_to_zero_over_keys():
+    """Each row of dS sums to zero (softmax), so sum_j dK_k[j] = 0 per head:
+    the property the long-sequence GPU test checks at full size."""
+    x = _case(29, 2, 2, 33, 8)
+    g = O.backward(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], x["lq1"], x["lk1"], x["lq2"], x["lk2"],
+                   x["lambda_init"], x["dout"], weight=x["weight"], eps=1e-5, causal=True)
+    for k in ("dk1", "dk2"):
+        assert np.max(np.abs(g[k].sum(axis=2))) < 1e-12 * max(1.0, np.max(np.abs(g[k])))
