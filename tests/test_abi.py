@@ -191,3 +191,19 @@ def test_lambda_bwd_validation(L):
         q[i] = None
         assert L.diffattn_lambda_bwd(*q[:4], 64, *q[4:], None) == b.EINVAL
     assert L.diffattn_lambda_bwd(*p[:4], 0, *p[4:], None) == b.EINVAL
+
+
+def test_training_bindings_refuse_host_tensors():
+    """The ctypes layer refuses tensors that are not on a HIP device before
+    anything reaches the library (no launch, no GPU needed)."""
+    import torch
+
+    t = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    v = torch.zeros(1, 1, 8, 128, dtype=torch.bfloat16)
+    lam = torch.zeros(1)
+    with pytest.raises(ValueError):
+        b.fwd_train(t, t, t, t, v, lam, 0.8)
+    with pytest.raises(ValueError):
+        b.bwd(t, t, t, t, v, v, torch.zeros(2, 1, 1, 8), torch.zeros(2, 1, 1, 8, 128), lam, 0.8)
+    with pytest.raises(ValueError):
+        b.lambda_bwd(torch.zeros(64), torch.zeros(64), torch.zeros(64), torch.zeros(64), lam)
