@@ -219,3 +219,15 @@ def test_backward_large_logits(dev, d):
     for k in ("dq1", "dk1", "dq2", "dk2", "dv"):
         assert np.all(np.isfinite(gr[k])), k
     _compare(gr, _oracle(x, True), ("dq1", "dk1", "dq2", "dk2", "dv", "dweight"))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [31, 32, 33, 63, 64, 65, 127, 128, 129])
+def test_backward_tile_boundaries(dev, d, N):
+    """Lengths on each side of the 32-row tiles and the 64/128-row blocks of
+    the dQ and dK/dV kernels."""
+    print(f"case bwd boundary d={d} N={N}", flush=True)
+    x = _inputs(1, 2, N, d, seed=4000 + N + d)
+    out, plain, lse, o12, gr = _run(x, dev, True)
+    assert torch.equal(out, plain)
+    _compare(gr, _oracle(x, True), ("dq1", "dk1", "dq2", "dk2", "dv", "dweight"))
