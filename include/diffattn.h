@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define DIFFATTN_ABI_VERSION 2
+#define DIFFATTN_ABI_VERSION 3
 
 #if defined(__GNUC__) || defined(__clang__)
 #define DIFFATTN_API __attribute__((visibility("default")))
@@ -197,6 +197,47 @@ DIFFATTN_API diffattn_status diffattn_bwd(diffattn_dtype dt, const void* q1, con
 DIFFATTN_API diffattn_status diffattn_lambda_bwd(const float* lq1, const float* lk1, const float* lq2,
                                     const float* lk2, int d, const float* dlambda, float* dlq1,
                                     float* dlk1, float* dlq2, float* dlk2, void* stream);
+
+/*
+ * fp8 (e4m3) query/key path: low-bit attention logits ("Differential
+ * Transformer" sample peer review, "Strengths", and the low-bit
+ * attention-logit figure it discusses, Fig. 8).  The format is OCP e4m3
+ * (bias 7, no infinities, largest finite value 448).
+ *
+ * diffattn_quantize_fp8_workspace_bytes -- device scratch bytes that
+ * diffattn_quantize_fp8 needs for n values (at most 4096; 0 for n < 0).
+ */
+DIFFATTN_API size_t diffattn_quantize_fp8_workspace_bytes(long long n);
+
+/*
+ * diffattn_quantize_fp8 -- per-tensor absmax quantisation of n bf16 values:
+ *   scale[0] = amax / 448 and codes[i] = e4m3(x[i] * (448 / amax)), with
+ *   amax = max |x|, float32 division and product, round to nearest even and
+ *   saturation at 448; an all-zero tensor gives scale 1 and zero codes.
+ *   x         : device bf16 [n], 16-byte aligned, finite values
+ *   codes     : device uint8 [n], 16-byte aligned, written in full
+ *   scale     : device fp32 [1], written
+ *   workspace : at least diffattn_quantize_fp8_workspace_bytes(n) bytes,
+ *               4-byte aligned; calls sharing it must be ordered on one stream.
+ * n = 0 launches nothing and leaves scale unwritten.
+ */
+DIFFATTN_API diffattn_status diffattn_quantize_fp8(const void* x, long long n, void* codes, float* scale,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * diffattn_fwd_fp8qk -- the prefill of diffattn_fwd (Eq. 1 then Eq. 3) with
+ * e4m3 queries and keys: the logits are (q . k) * sq * sk / sqrt(d), the
+ * products of e4m3 values summed exactly into fp32 by the fp8 matrix cores.
+ *   q1, k1, q2, k2 : device e4m3 bytes [B, H, N, d], d = 128 only
+ *   qk_scale       : device fp32 [4]: the scales of q1, k1, q2, k2 (e.g. from
+ *                    diffattn_quantize_fp8)
+ *   v, out         : device bf16 [B, H, N, 2d]
+ *   the rest       : as for diffattn_fwd with dt = DIFFATTN_BF16
+ */
+DIFFATTN_API diffattn_status diffattn_fwd_fp8qk(const void* q1, const void* k1, const void* q2, const void* k2,
+                                   const float* qk_scale, const void* v, void* out, int B, int H, int N,
+                                   int d, const float* lambda, float lambda_init,
+                                   const float* norm_weight, float eps, unsigned flags, void* stream);
 
 /* Static English text for a status code (never NULL). */
 DIFFATTN_API const char* diffattn_strerror(diffattn_status status);

@@ -36,8 +36,9 @@ def L():
 def test_header_declares_the_abi():
     assert declared_symbols() == sorted([
         "diffattn_abi_version", "diffattn_bwd", "diffattn_bwd_workspace_bytes", "diffattn_decode",
-        "diffattn_decode_workspace_bytes", "diffattn_fwd", "diffattn_fwd_train", "diffattn_lambda",
-        "diffattn_lambda_bwd", "diffattn_strerror"])
+        "diffattn_decode_workspace_bytes", "diffattn_fwd", "diffattn_fwd_fp8qk", "diffattn_fwd_train",
+        "diffattn_lambda", "diffattn_lambda_bwd", "diffattn_quantize_fp8", "diffattn_quantize_fp8_workspace_bytes",
+        "diffattn_strerror"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -51,7 +52,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_strerror(L):
-    assert L.diffattn_abi_version() == 2
+    assert L.diffattn_abi_version() == 3
     for code in range(5):
         assert L.diffattn_strerror(code)
     assert L.diffattn_strerror(99) == b"unknown status"
@@ -182,6 +183,40 @@ def test_bwd_validation(L):
     # sizes whose 32-bit row offsets would overflow
     assert _bwd(L, B=1 << 12, H=1 << 12, N=1 << 6) == b.EINVAL
     assert _bwd(L, N=0) == b.OK
+
+
+def _fp8(L, d=128, B=1, H=1, N=8, ptrs=(A16,) * 6, scale=A16, flags=b.CAUSAL, eps=1e-5):
+    q1, k1, q2, k2, v, out = ptrs
+    return L.diffattn_fwd_fp8qk(q1, k1, q2, k2, scale, v, out, B, H, N, d, A16, 0.8, None, eps, flags, None)
+
+
+def test_fwd_fp8qk_validation(L):
+    for d in (16, 32, 64, 256):
+        assert _fp8(L, d=d) == b.EUNSUPPORTED  # the fp8 product is 128 deep
+    assert _fp8(L, scale=None) == b.EINVAL
+    assert _fp8(L, scale=A16 + 2) == b.EINVAL
+    assert _fp8(L, flags=8) == b.EINVAL
+    assert _fp8(L, eps=-1.0) == b.EINVAL
+    assert _fp8(L, N=-1) == b.EINVAL
+    for i in range(6):
+        p = [A16] * 6
+        p[i] = MIS
+        assert _fp8(L, ptrs=p) == b.EINVAL, i
+    assert _fp8(L, N=0, scale=None) == b.OK
+
+
+def test_quantize_fp8_validation(L):
+    assert L.diffattn_quantize_fp8_workspace_bytes(-1) == 0
+    assert L.diffattn_quantize_fp8_workspace_bytes(1) == 4
+    assert L.diffattn_quantize_fp8_workspace_bytes(1 << 40) == 4096
+    q = L.diffattn_quantize_fp8
+    assert q(A16, -1, A16, A16, A16, 4096, None) == b.EINVAL
+    assert q(A16, 0, None, None, None, 0, None) == b.OK
+    assert q(MIS, 100, A16, A16, A16, 4096, None) == b.EINVAL
+    assert q(A16, 100, MIS, A16, A16, 4096, None) == b.EINVAL
+    assert q(A16, 100, A16, None, A16, 4096, None) == b.EINVAL
+    assert q(A16, 100, A16, A16, None, 4096, None) == b.EWORKSPACE
+    assert q(A16, 1 << 30, A16, A16, A16, 16, None) == b.EWORKSPACE
 
 
 def test_lambda_bwd_validation(L):

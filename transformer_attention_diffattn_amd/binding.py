@@ -53,6 +53,12 @@ def lib() -> ctypes.CDLL:
         L.diffattn_bwd.restype = i
         L.diffattn_lambda_bwd.argtypes = [vp, vp, vp, vp, i, vp, vp, vp, vp, vp, vp]
         L.diffattn_lambda_bwd.restype = i
+        L.diffattn_quantize_fp8_workspace_bytes.argtypes = [ctypes.c_longlong]
+        L.diffattn_quantize_fp8_workspace_bytes.restype = sz
+        L.diffattn_quantize_fp8.argtypes = [vp, ctypes.c_longlong, vp, vp, vp, sz, vp]
+        L.diffattn_quantize_fp8.restype = i
+        L.diffattn_fwd_fp8qk.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, vp, f, vp, f, u, vp]
+        L.diffattn_fwd_fp8qk.restype = i
         L.diffattn_abi_version.argtypes = []
         L.diffattn_abi_version.restype = i
         _lib = L
@@ -242,3 +248,68 @@ def lambda_bwd(lq1, lk1, lq2, lk2, dlambda):
     _check(lib().diffattn_lambda_bwd(_ptr(lq1), _ptr(lk1), _ptr(lq2), _ptr(lk2), lq1.numel(), _ptr(dlambda),
                                      *[_ptr(o) for o in outs], _stream(lq1.device)), "diffattn_lambda_bwd")
     return tuple(outs)
+
+
+def quantize_fp8_workspace_bytes(n: int) -> int:
+    return int(lib().diffattn_quantize_fp8_workspace_bytes(n))
+
+
+def quantize_fp8(x, codes=None, scale=None, workspace=None):
+    """Per-tensor absmax e4m3 quantisation of a bf16 tensor: returns
+    (codes uint8 of x's shape, scale fp32 [1]); scale may be a 1-element view
+    of a larger fp32 tensor."""
+    _dev(x, "x")
+    if x.dtype != torch.bfloat16:
+        raise ValueError("x must be bfloat16")
+    n = x.numel()
+    if codes is None:
+        codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    else:
+        _dev(codes, "codes")
+        if codes.dtype != torch.uint8 or codes.numel() != n:
+            raise ValueError("codes must be uint8 with x's element count")
+    if scale is None:
+        scale = torch.empty(1, dtype=torch.float32, device=x.device)
+    elif scale.dtype != torch.float32 or scale.numel() != 1 or scale.device.type != "cuda":
+        raise ValueError("scale must be one fp32 element on a HIP device")
+    need = quantize_fp8_workspace_bytes(n)
+    if workspace is None:
+        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=x.device)
+    _check(lib().diffattn_quantize_fp8(_ptr(x), n, _ptr(codes), _ptr(scale), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), _stream(x.device)),
+           "diffattn_quantize_fp8")
+    return codes, scale
+
+
+def fwd_fp8qk(q1, k1, q2, k2, qk_scale, v, lam_t, lambda_init: float, weight=None, eps: float = 1e-5,
+              causal: bool = True, norm: bool = True, out=None) -> torch.Tensor:
+    """Prefill with e4m3 queries/keys (uint8 [B,H,N,128]) and their scales
+    (device fp32 [4]: q1, k1, q2, k2); v bf16 [B,H,N,256] -> out bf16."""
+    for n, t in (("q1", q1), ("k1", k1), ("q2", q2), ("k2", k2), ("qk_scale", qk_scale), ("v", v),
+                 ("lambda", lam_t)):
+        _dev(t, n)
+    B, H, N, d = q1.shape
+    for n, t in (("q1", q1), ("k1", k1), ("q2", q2), ("k2", k2)):
+        if t.shape != q1.shape or t.dtype != torch.uint8:
+            raise ValueError(f"{n} must be uint8 e4m3 codes of q1's shape")
+    if qk_scale.dtype != torch.float32 or qk_scale.numel() != 4:
+        raise ValueError("qk_scale must be fp32 [4]")
+    if v.shape != (B, H, N, 2 * d) or v.dtype != torch.bfloat16:
+        raise ValueError("v must be bf16 [B,H,N,2d]")
+    if lam_t.dtype != torch.float32:
+        raise ValueError("lambda must be fp32")
+    if weight is not None:
+        _dev(weight, "weight")
+        if weight.dtype != torch.float32 or weight.shape != (2 * d,):
+            raise ValueError("weight must be fp32 [2d]")
+    if out is None:
+        out = torch.empty_like(v)
+    else:
+        _dev(out, "out")
+        if out.shape != v.shape or out.dtype != v.dtype:
+            raise ValueError("out must match v")
+    flags = (CAUSAL if causal else 0) | (0 if norm else NO_NORM)
+    _check(lib().diffattn_fwd_fp8qk(_ptr(q1), _ptr(k1), _ptr(q2), _ptr(k2), _ptr(qk_scale), _ptr(v), _ptr(out),
+                                    B, H, N, d, _ptr(lam_t), float(lambda_init), _ptr(weight), float(eps),
+                                    flags, _stream(q1.device)), "diffattn_fwd_fp8qk")
+    return out

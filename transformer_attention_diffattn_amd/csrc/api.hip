@@ -76,9 +76,10 @@ diffattn_status diffattn_lambda(const float* lq1, const float* lk1, const float*
 static diffattn_status fwd_impl(diffattn_dtype dt, const void* q1, const void* k1, const void* q2, const void* k2,
                                 const void* v, void* out, int B, int H, int N, int d, const float* lambda,
                                 float lambda_init, const float* norm_weight, float eps, unsigned flags,
-                                float* lse, float* osave, void* stream) {
+                                float* lse, float* osave, void* stream, const float* qk_scale = nullptr) {
   if (dt != DIFFATTN_FP32 && dt != DIFFATTN_BF16) return DIFFATTN_EUNSUPPORTED;
   if (!supported_d(d)) return DIFFATTN_EUNSUPPORTED;
+  if (qk_scale && (dt != DIFFATTN_BF16 || d != 128)) return DIFFATTN_EUNSUPPORTED;
   if (B < 0 || H < 0 || N < 0) return DIFFATTN_EINVAL;
   if (flags & ~(DIFFATTN_CAUSAL | DIFFATTN_NO_NORM)) return DIFFATTN_EINVAL;
   const bool norm = !(flags & DIFFATTN_NO_NORM);
@@ -88,6 +89,7 @@ static diffattn_status fwd_impl(diffattn_dtype dt, const void* q1, const void* k
     return DIFFATTN_EINVAL;
   if (!ok_ptr4(lambda)) return DIFFATTN_EINVAL;
   if (norm_weight && !aligned(norm_weight, 4)) return DIFFATTN_EINVAL;
+  if (qk_scale && !ok_ptr4(qk_scale)) return DIFFATTN_EINVAL;
   const long long BH = (long long)B * H;
   const bool bf16 = dt == DIFFATTN_BF16;
   const int bm = diffattn::prefill_block_rows(bf16, d);
@@ -113,7 +115,10 @@ static diffattn_status fwd_impl(diffattn_dtype dt, const void* q1, const void* k
   a.c = (float)(1.4426950408889634 / sqrt((double)d));
   a.lse = lse;
   a.osave = osave;
-  hipError_t e = diffattn::launch_prefill(bf16, d, (flags & DIFFATTN_CAUSAL) != 0, norm, a, (hipStream_t)stream);
+  a.qk_scale = qk_scale;
+  const bool causal = (flags & DIFFATTN_CAUSAL) != 0;
+  hipError_t e = qk_scale ? diffattn::launch_prefill_fp8qk(causal, norm, a, (hipStream_t)stream)
+                          : diffattn::launch_prefill(bf16, d, causal, norm, a, (hipStream_t)stream);
   return e == hipSuccess ? DIFFATTN_OK : DIFFATTN_EHIP;
 }
 
@@ -123,6 +128,32 @@ diffattn_status diffattn_fwd(diffattn_dtype dt, const void* q1, const void* k1, 
                              void* stream) {
   return fwd_impl(dt, q1, k1, q2, k2, v, out, B, H, N, d, lambda, lambda_init, norm_weight, eps, flags, nullptr,
                   nullptr, stream);
+}
+
+diffattn_status diffattn_fwd_fp8qk(const void* q1, const void* k1, const void* q2, const void* k2,
+                                   const float* qk_scale, const void* v, void* out, int B, int H, int N, int d,
+                                   const float* lambda, float lambda_init, const float* norm_weight, float eps,
+                                   unsigned flags, void* stream) {
+  if (d != 128) return DIFFATTN_EUNSUPPORTED;
+  if ((long long)B * H * N > 0 && !ok_ptr4(qk_scale)) return DIFFATTN_EINVAL;
+  return fwd_impl(DIFFATTN_BF16, q1, k1, q2, k2, v, out, B, H, N, d, lambda, lambda_init, norm_weight, eps, flags,
+                  nullptr, nullptr, stream, qk_scale);
+}
+
+size_t diffattn_quantize_fp8_workspace_bytes(long long n) {
+  if (n < 0) return 0;
+  return (size_t)diffattn::quant_partial_blocks(n) * sizeof(float);
+}
+
+diffattn_status diffattn_quantize_fp8(const void* x, long long n, void* codes, float* scale, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  if (n < 0) return DIFFATTN_EINVAL;
+  if (n == 0) return DIFFATTN_OK;
+  if (!ok_ptr16(x) || !ok_ptr16(codes) || !ok_ptr4(scale)) return DIFFATTN_EINVAL;
+  if (workspace == nullptr || !aligned(workspace, 4) || workspace_bytes < diffattn_quantize_fp8_workspace_bytes(n))
+    return DIFFATTN_EWORKSPACE;
+  hipError_t e = diffattn::launch_quantize_fp8(x, n, (float*)workspace, (uint8_t*)codes, scale, (hipStream_t)stream);
+  return e == hipSuccess ? DIFFATTN_OK : DIFFATTN_EHIP;
 }
 
 diffattn_status diffattn_fwd_train(diffattn_dtype dt, const void* q1, const void* k1, const void* q2,

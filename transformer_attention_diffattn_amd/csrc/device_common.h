@@ -12,6 +12,7 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+typedef __attribute__((ext_vector_type(8))) int i32x8;  // 32 fp8 values
 
 // log2(e): softmax weights are formed as 2^(s * log2(e)/sqrt(d) - m) so that
 // one FMA and one v_exp_f32 give exp((s - m')/sqrt(d)).
@@ -36,6 +37,15 @@ constexpr int kStoreStreaming = 2;
 
 __device__ __forceinline__ f32x4 mfma16x16x32_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16x16x128 product of e4m3 operands (both format fields 0 = fp8 e4m3) with
+// unit block scales (exponent byte 127 = 2^0).  Lane L holds row L % 16 of
+// A (and of B) with 32 of its 128 reduction elements; any assignment of
+// reduction elements to lane groups and bytes gives the same product as long
+// as A and B use the same one.  C has the 16x16x32 bf16 product's layout.
+__device__ __forceinline__ f32x4 mfma16x16x128_fp8(i32x8 a, i32x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
 __device__ __forceinline__ f32x4 mfma16x16x4_f32(float a, float b, f32x4 c) {

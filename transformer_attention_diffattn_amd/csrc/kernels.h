@@ -23,6 +23,7 @@ struct PrefillArgs {
   float c;              // log2(e) / sqrt(d)
   float* lse;           // training forward: [2][BH][N] log2-sum-exp per map, or null
   float* osave;         // training forward: [2][BH][N][2d] per-map O / l, or null
+  const float* qk_scale;  // fp8 queries/keys: device [4] scales of q1, k1, q2, k2; else null
 };
 
 struct DecodeArgs {
@@ -81,6 +82,14 @@ hipError_t launch_lambda(const float* lq1, const float* lk1, const float* lq2, c
 
 hipError_t launch_prefill(bool bf16, int d, bool causal, bool norm, const PrefillArgs& a,
                           hipStream_t stream);
+// d = 128, e4m3 q1/k1/q2/k2 (a.qk_scale set), bf16 v and output
+hipError_t launch_prefill_fp8qk(bool causal, bool norm, const PrefillArgs& a, hipStream_t stream);
+
+// Per-tensor absmax e4m3 quantisation of n bf16 values: partial maxima of
+// quant_partial_blocks(n) workgroups, then the scale and the codes.
+int quant_partial_blocks(long long n);
+hipError_t launch_quantize_fp8(const void* x, long long n, float* partial, uint8_t* codes, float* scale,
+                               hipStream_t stream);
 
 // Split plan for decode: number of splits and keys per split.
 void decode_plan(int B, int H, int L, int d, int* S, int* chunk);

@@ -121,9 +121,13 @@ struct Bf16Cfg {
   static constexpr int V_AHEAD = 2;  // V^T fragments
 };
 
-template <int D>
+// F8: queries and keys are e4m3 bytes (QK^T on the 16x16x128 fp8 product,
+// d = 128 only); a K tile then fills the first half of its slot.
+template <int D, bool F8 = false>
 struct Bf16Tile {
+  static_assert(!F8 || D == 128, "the fp8 QK^T product is 128 deep");
   static constexpr int DV = 2 * D;
+  static constexpr int KB = F8 ? 1 : 2;  // bytes per query/key element
   static constexpr int WAVES = Bf16Cfg<D>::WAVES;  // row groups x 2 maps
   static constexpr int SUB = Bf16Cfg<D>::SUB;      // 16-row sub-tiles per wave
   static constexpr int BM = 16 * SUB * (WAVES / 2);
@@ -134,16 +138,16 @@ struct Bf16Tile {
   static constexpr int V_AHEAD = Bf16Cfg<D>::V_AHEAD;
   static_assert(STAGES >= (PIPE ? 3 : 2), "stage ring of the tile loop");
   static constexpr int PV_FENCE = Bf16Cfg<D>::PV_FENCE;
-  static constexpr int KS = (D + 31) / 32;  // 32-wide k-steps of the QK^T MFMA
+  static constexpr int KS = F8 ? 1 : (D + 31) / 32;  // k-steps of the QK^T MFMA
   static constexpr int NB = BN / 16;        // 16-key score blocks per tile
   static constexpr int NC = BN / 32;        // 32-key PV k-steps per tile
   static constexpr int CB = DV / 16;        // 16-channel output blocks
-  static constexpr int NCH = D / 8;         // 16-byte chunks per K row
+  static constexpr int NCH = D * KB / 16;   // 16-byte chunks per K row
   static constexpr int RPK = NCH >= 16 ? 1 : 16 / NCH;  // K rows per 256 bytes
   static constexpr int KSEG = BN * NCH / 64;            // 1 KB segments per K tile
   static constexpr int VSEG = CB * BN / 32;             // 1 KB = 32 keys of one channel block
   static constexpr int NSEG = 2 * KSEG + VSEG;
-  static constexpr int KTILE = BN * D;  // elements
+  static constexpr int KTILE = BN * D;  // 16-bit elements (slot of one K tile)
   static constexpr int VTILE = BN * DV;
   static constexpr int STAGE = 2 * KTILE + VTILE;
   static_assert(NSEG % (WAVES / 2) == 0, "segments split evenly over the loading waves");
@@ -171,10 +175,25 @@ __device__ __forceinline__ float max4_groups(float x) {
   return max_f32(u32_as_f32(q[0]), u32_as_f32(q[1]));
 }
 
+// QK^T operand fragments: 8 bf16, or 32 e4m3 bytes
+__device__ __forceinline__ f32x4 mma_qk(bf16x8 a, bf16x8 b, f32x4 c) { return mfma16x16x32_bf16(a, b, c); }
+__device__ __forceinline__ f32x4 mma_qk(i32x8 a, i32x8 b, f32x4 c) { return mfma16x16x128_fp8(a, b, c); }
+__device__ __forceinline__ i32x8 cat_i32x8(u32x4 lo, u32x4 hi) {
+  i32x8 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r[i] = (int)lo[i];
+    r[4 + i] = (int)hi[i];
+  }
+  return r;
+}
+
 // SAVE: the training forward (also writes the per-map statistics).
-template <int D, bool CAUSAL, bool NORM, bool SAVE>
+// F8: e4m3 queries and keys with per-tensor scales (a.qk_scale).
+template <int D, bool CAUSAL, bool NORM, bool SAVE, bool F8>
 __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(PrefillArgs a) {
-  using T = Bf16Tile<D>;
+  using T = Bf16Tile<D, F8>;
+  using QFrag = std::conditional_t<F8, i32x8, bf16x8>;
   constexpr int DV = T::DV, BN = T::BN, KS = T::KS, NB = T::NB, NC = T::NC, CB = T::CB, SUB = T::SUB;
   constexpr int NCH = T::NCH, KSEG = T::KSEG, KTILE = T::KTILE;
   constexpr int RG = T::WAVES / 2;  // row groups
@@ -193,7 +212,8 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
   const int lr = lane & 15;  // query column of the 16x16 blocks owned by this lane
   const int lg = lane >> 4;  // lane group: rows 4*lg..4*lg+3 of each block
   const int N = a.N;
-  const float c = a.c;
+  // fp8: the dequantisation scales of this wave's map fold into the logit scale
+  const float c = F8 ? a.c * (mp ? a.qk_scale[2] * a.qk_scale[3] : a.qk_scale[0] * a.qk_scale[1]) : a.c;
   const float lam = *a.lambda;
   for (int i = threadIdx.x; i < DV; i += blockDim.x) wsh[i] = a.norm_w ? a.norm_w[i] : 1.0f;
 
@@ -230,8 +250,18 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
   auto head_row = [&](const Item& it) { return (size_t)it.bh * (size_t)N; };
 
   // Q^T fragments (B operand of S^T = K Q^T): dims 32ks+8lg..+7 of the row
-  bf16x8 qf[SUB][KS];
+  // (fp8: bytes 32lg..+31 of the row)
+  QFrag qf[SUB][KS];
   auto load_q = [&](const Item& it) {
+    if constexpr (F8) {
+      const uint8_t* Qm = (const uint8_t*)(mp ? a.q2 : a.q1) + head_row(it) * D;
+#pragma unroll
+      for (int u = 0; u < SUB; ++u) {
+        const uint8_t* qp = Qm + (size_t)min(it.qw0 + 16 * u + lr, N - 1) * D + 32 * lg;
+        qf[u][0] = cat_i32x8(ld16(qp), ld16(qp + 16));
+      }
+      return;
+    } else {
     const uint16_t* Qm = (const uint16_t*)(mp ? a.q2 : a.q1) + head_row(it) * D;
 #pragma unroll
     for (int u = 0; u < SUB; ++u) {
@@ -241,6 +271,7 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
         const int dc = 32 * ks + 8 * lg;
         qf[u][ks] = as_bf16x8(dc < D ? ld16(Qm + (size_t)qrow * D + dc) : zero_u32x4());
       }
+    }
     }
   };
 
@@ -269,7 +300,7 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
       seg_sel[i] = seg / KSEG;
       seg_lds[i] = 2u * (uint32_t)((seg / KSEG) * KTILE + sg * 512);
       seg_row[i] = r;
-      seg_off[i] = 2u * (uint32_t)(r * D + 8 * T::kchunk(r, lane % NCH));
+      seg_off[i] = (uint32_t)(r * D * T::KB + 16 * T::kchunk(r, lane % NCH));
     } else {
       // segment sg: keys 32*(sg % (BN/32)).. of channel block sg / (BN/32);
       // lane: key +lane/2, channels +8*(lane&1)
@@ -285,8 +316,8 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
   auto issue_tile = [&](int buf, const Item& it, int kt) {
     const int kb = kt * BN;
     const size_t row0 = head_row(it) + (size_t)kb;
-    const char* bk1 = (const char*)a.k1 + row0 * (2 * D);
-    const char* bk2 = (const char*)a.k2 + row0 * (2 * D);
+    const char* bk1 = (const char*)a.k1 + row0 * (T::KB * D);
+    const char* bk2 = (const char*)a.k2 + row0 * (T::KB * D);
     const char* bv = (const char*)a.v + row0 * (2 * DV);
     const uint32_t lds0 = lds_stages + (uint32_t)(buf * T::STAGE * 2);
     if (wave >= LOADERS) return;
@@ -298,7 +329,7 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
       // ragged last tile: rows past N - 1 read row N - 1 instead
 #pragma unroll
       for (int i = 0; i < SPW; ++i) {
-        const uint32_t row_bytes = seg_sel[i] == 2 ? 2 * DV : 2 * D;
+        const uint32_t row_bytes = seg_sel[i] == 2 ? 2 * DV : T::KB * D;
         const uint32_t off = seg_off[i] - (uint32_t)max(0, kb + seg_row[i] - (N - 1)) * row_bytes;
         lds_dma16_s(seg_sel[i] == 0 ? bk1 : (seg_sel[i] == 1 ? bk2 : bv), off, lds0 + seg_lds[i]);
       }
@@ -312,6 +343,17 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
 
   using Scores = float[SUB][4 * NB];  // this lane's raw scores of one tile
   using PFrags = bf16x8[NC][SUB];      // P^T fragments of one tile
+
+  // K fragment (A operand) of key row kr of the K tile at ks_, k-step ks
+  auto kfrag = [&](const uint16_t* ks_, int kr, int ks) -> QFrag {
+    if constexpr (F8) {
+      const uint8_t* row = (const uint8_t*)ks_ + kr * D;
+      return cat_i32x8(ld16(row + 16 * T::kchunk(kr, 2 * lg)), ld16(row + 16 * T::kchunk(kr, 2 * lg + 1)));
+    } else {
+      const int ch = 4 * ks + lg;
+      return as_bf16x8(ch < NCH ? ld16(ks_ + kr * D + 8 * T::kchunk(kr, ch)) : zero_u32x4());
+    }
+  };
 
   // S^T = K Q^T for both sub-tiles; block b of sc holds keys 16b+4lg+j.
   // MASK: the tile holds keys past some row's diagonal or past N; those
@@ -336,10 +378,9 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
       for (int u = 0; u < SUB; ++u) acc[u] = zero_f32x4();
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const int ch = 4 * ks + lg;
-        const bf16x8 ka = as_bf16x8(ch < NCH ? ld16(ks_ + kr * D + 8 * T::kchunk(kr, ch)) : zero_u32x4());
+        const QFrag ka = kfrag(ks_, kr, ks);
 #pragma unroll
-        for (int u = 0; u < SUB; ++u) acc[u] = mfma16x16x32_bf16(ka, qf[u][ks], acc[u]);
+        for (int u = 0; u < SUB; ++u) acc[u] = mma_qk(ka, qf[u][ks], acc[u]);
       }
 #pragma unroll
       for (int u = 0; u < SUB; ++u)
@@ -420,13 +461,9 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
   // work of one tile and the VALU work of the other stay interleaved.
 
   // K fragments (A operand) of 16-key block b
-  auto load_kf = [&](const uint16_t* ks_, int b, bf16x8 (&kf)[KS]) {
-    const int kr = 16 * b + lr;
+  auto load_kf = [&](const uint16_t* ks_, int b, QFrag (&kf)[KS]) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int ch = 4 * ks + lg;
-      kf[ks] = as_bf16x8(ch < NCH ? ld16(ks_ + kr * D + 8 * T::kchunk(kr, ch)) : zero_u32x4());
-    }
+    for (int ks = 0; ks < KS; ++ks) kf[ks] = kfrag(ks_, 16 * b + lr, ks);
   };
   // V^T fragment j = (32-key chunk j / CB, channel block j % CB)
   auto load_vf = [&](const uint16_t* vs, int j) {
@@ -471,7 +508,7 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
   // current tile (t -> 2^t in place).
   auto phase_a = [&](const uint16_t* ks_, Scores& sn, Scores& t) {
     constexpr int KA = T::K_AHEAD;  // K blocks read ahead
-    bf16x8 kf[KA + 1][KS];
+    QFrag kf[KA + 1][KS];
 #pragma unroll
     for (int b = 0; b < KA && b < NB; ++b) load_kf(ks_, b, kf[b]);
 #pragma unroll
@@ -483,7 +520,7 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int u = 0; u < SUB; ++u) acc[u] = mfma16x16x32_bf16(kf[b % (KA + 1)][ks], qf[u][ks], acc[u]);
+        for (int u = 0; u < SUB; ++u) acc[u] = mma_qk(kf[b % (KA + 1)][ks], qf[u][ks], acc[u]);
 #pragma unroll
       for (int u = 0; u < SUB; ++u)
 #pragma unroll
@@ -1170,7 +1207,7 @@ static hipError_t compute_units(int* ncu) {
   return e;
 }
 
-template <int D, bool C, bool NM, bool SV>
+template <int D, bool C, bool NM, bool SV, bool F8 = false>
 static hipError_t launch_one(bool bf16, const PrefillArgs& a, hipStream_t s) {
   const long long items = (long long)a.n_qtiles * (long long)a.BH;
   const dim3 block(prefill_block_threads(bf16, D));
@@ -1180,8 +1217,8 @@ static hipError_t launch_one(bool bf16, const PrefillArgs& a, hipStream_t s) {
     const hipError_t e = compute_units(&ncu);
     if (e != hipSuccess) return e;
     const long long grid = items < ncu ? items : (ncu > 0 ? ncu : 1);
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, C, NM, SV>), dim3((unsigned)grid), block, 0, s, a);
-  } else if constexpr (!SV) {
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, C, NM, SV, F8>), dim3((unsigned)grid), block, 0, s, a);
+  } else if constexpr (!SV && !F8) {
     hipLaunchKernelGGL((prefill_f32_kernel<D, C, NM>), dim3((unsigned)items), block, 0, s, a);
   } else {
     return hipErrorInvalidValue;  // no fp32 training forward
@@ -1215,6 +1252,14 @@ hipError_t launch_prefill(bool bf16, int d, bool causal, bool norm, const Prefil
     case 128: return launch_d<128>(bf16, causal, norm, save, a, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_prefill_fp8qk(bool causal, bool norm, const PrefillArgs& a, hipStream_t stream) {
+  if (causal)
+    return norm ? launch_one<128, true, true, false, true>(true, a, stream)
+                : launch_one<128, true, false, false, true>(true, a, stream);
+  return norm ? launch_one<128, false, true, false, true>(true, a, stream)
+              : launch_one<128, false, false, false, true>(true, a, stream);
 }
 
 }  // namespace diffattn
