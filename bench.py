@@ -29,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
+PEAK_FP8_TFLOPS = 5033.2    # MI355X dense fp8 MFMA (twice the bf16 rate)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "diff-attn fwd TFLOP/s & % bf16 MFMA peak (prefill); decode HBM GB/s & % peak"
 
@@ -225,6 +226,72 @@ where dV and dK are also computed apart)."""
     return leg
 
 
+def fp8_leg(args, stream, torch, da, W):
+    """The fp8 query/key prefill (diffattn_fwd_fp8qk) against the bf16 prefill
+    on the same d = 128 workload, and the quantiser that feeds it.  Its peak
+    is that of its mix: per causal pair 4 d flops of QK^T at the fp8 rate and
+    8 d of PV at the bf16 rate."""
+    w = W.WORKLOADS["layer3b_bf16_b2h12n4096d128"]
+    dev = torch.device("cuda:0")
+    x = W.workload_inputs(w.name, device=dev)
+    lam_t = da.lam(x["lq1"], x["lk1"], x["lq2"], x["lk2"], x["lambda_init"])
+    names = ("q1", "k1", "q2", "k2")
+    n = x["q1"].numel()
+    codes = {k: torch.empty(x[k].shape, dtype=torch.uint8, device=dev) for k in names}
+    scales = torch.empty(4, dtype=torch.float32, device=dev)
+    qws = torch.empty(max(4, da.quantize_fp8_workspace_bytes(n)), dtype=torch.uint8, device=dev)
+    out8 = torch.empty_like(x["v"])
+    out16 = torch.empty_like(x["v"])
+
+    def quant():
+        for i, k in enumerate(names):
+            da.quantize_fp8(x[k], codes=codes[k], scale=scales[i:i + 1], workspace=qws)
+
+    def f8():
+        da.fwd_fp8qk(codes["q1"], codes["k1"], codes["q2"], codes["k2"], scales, x["v"], lam_t,
+                     x["lambda_init"], eps=x["eps"], causal=w.causal, out=out8)
+
+    def f16():
+        da.fwd(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam_t, x["lambda_init"], eps=x["eps"],
+               causal=w.causal, out=out16)
+
+    quant()
+    f8()
+    torch.cuda.synchronize()
+    eager = out8.clone()
+    R = 10
+    steps = max(R, args.fp8_steps // R * R)
+    ms = {}
+    for name, fn, pre in (("quant", quant, 0.2), ("fp8", f8, min(0.5, args.prewarm_s)),
+                          ("bf16", f16, min(0.5, args.prewarm_s))):
+        g = _graph(lambda fn=fn: [fn() for _ in range(R)], torch)
+        _prewarm(g.replay, pre, torch)
+        ms[name] = _timed(g.replay, steps // R, stream, torch) / steps
+    if not torch.equal(out8, eager):
+        raise RuntimeError("graph replay of the fp8 prefill differs from the eager call")
+    flops = 12.0 * w.d * w.pairs() * w.B * w.H
+    peak = 12.0 / (4.0 / PEAK_FP8_TFLOPS + 8.0 / PEAK_BF16_TFLOPS)
+    achieved = flops / (ms["fp8"] * 1e-3) / 1e12
+    qbytes = 4 * 3 * n  # per tensor: n bf16 read, n codes written
+    qgbs = qbytes / (ms["quant"] * 1e-3) / 1e9
+    return {
+        "workload": w.name, "ms_per_step": round(ms["fp8"], 4), "tflops": round(achieved, 2),
+        "bf16_prefill_ms": round(ms["bf16"], 4),
+        "bf16_prefill_tflops": round(flops / (ms["bf16"] * 1e-3) / 1e12, 2),
+        "speedup_vs_bf16": round(ms["bf16"] / ms["fp8"], 3),
+        "roofline": {"bound": "mfma", "kernel": "prefill_bf16_kernel<128,causal,norm,fp8 QK^T>",
+                     "achieved": round(achieved, 2), "peak": round(peak, 1), "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4),
+                     "traffic": _traffic("prefill_fp8qk_layer3b", "prefill.hip"),
+                     "peak_mix": "QK^T 4 d flops/pair at fp8 5033.2, PV 8 d at bf16 2516.6 TFLOP/s"},
+        "quantize": {"ms_per_call": round(ms["quant"] / 4, 4), "tensors": 4,
+                     "roofline": {"bound": "hbm", "kernel": "amax_partial_kernel + quantize_kernel",
+                                  "achieved": round(qgbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                  "frac": round(qgbs / PEAK_HBM_GBS, 4), "traffic": None,
+                                  "algorithmic_bytes": qbytes}},
+    }
+
+
 def cpu_backward(x, w, dout, budget_s: float):
     """The oracle's backward as it stands, on whole heads of the same inputs,
     until ``budget_s`` seconds are spent; priced at 20 d flops per pair."""
@@ -265,6 +332,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true", help="skip the decode leg")
     ap.add_argument("--no-bwd", action="store_true", help="skip the training (backward) leg")
     ap.add_argument("--bwd-steps", type=int, default=40)
+    ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 query/key prefill leg")
+    ap.add_argument("--fp8-steps", type=int, default=40)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of CPU oracle time")
     ap.add_argument("--no-ref-gemm", action="store_true",
@@ -399,6 +468,14 @@ def main():
         except Exception as e:  # noqa: BLE001
             print(f"training leg failed: {e!r}", file=sys.stderr, flush=True)
             res["backward"] = {"error": repr(e)}
+
+    # ---------------- fp8 query/key prefill (d = 128)
+    if not args.no_fp8:
+        try:
+            res["fp8_qk"] = fp8_leg(args, stream, torch, da, W)
+        except Exception as e:  # noqa: BLE001
+            print(f"fp8 leg failed: {e!r}", file=sys.stderr, flush=True)
+            res["fp8_qk"] = {"error": repr(e)}
 
     if not args.no_ref_gemm:
         g = reference_gemm(torch, dev)
