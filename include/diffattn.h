@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define DIFFATTN_ABI_VERSION 3
+#define DIFFATTN_ABI_VERSION 4
 
 #if defined(__GNUC__) || defined(__clang__)
 #define DIFFATTN_API __attribute__((visibility("default")))
@@ -238,6 +238,36 @@ DIFFATTN_API diffattn_status diffattn_fwd_fp8qk(const void* q1, const void* k1, 
                                    const float* qk_scale, const void* v, void* out, int B, int H, int N,
                                    int d, const float* lambda, float lambda_init,
                                    const float* norm_weight, float eps, unsigned flags, void* stream);
+
+/*
+ * Projections either side of the attention ("Differential attention" page,
+ * section "How it's wired": each head's query and key projections are split
+ * into halves Q1/K1 and Q2/K2; "Differential Transformer" sample peer
+ * review, "Strengths": heads halved, h = d_model / 2d).  Weights use the
+ * linear-layer layout W[out_features, in_features] (y = x W^T), no bias.
+ * bf16 inputs and outputs, fp32 accumulation, outputs rounded to nearest
+ * even.  All pointers are device memory, 16-byte aligned, not aliased.
+ *
+ * diffattn_in_proj -- [Q | K | V] = x [W_Q; W_K; W_V]^T with the head split:
+ *   x      : [B, N, d_model], d_model a multiple of 8
+ *   w_qkv  : [3 * H * 2d, d_model]: rows of W_Q, then W_K, then W_V; head h
+ *            owns rows h*2d .. h*2d + 2d - 1 of each, of which the first d of
+ *            W_Q (W_K) give Q1 (K1) and the last d give Q2 (K2)
+ *   q1, k1, q2, k2 : [B, H, N, d] written; v : [B, H, N, 2d] written
+ *   d in {16, 32, 64, 128}; B * N <= 8388480.
+ */
+DIFFATTN_API diffattn_status diffattn_in_proj(const void* x, const void* w_qkv, int B, int N, int d_model, int H,
+                                 int d, void* q1, void* k1, void* q2, void* k2, void* v, void* stream);
+
+/*
+ * diffattn_out_proj -- y = Concat_h(o[:, h]) W_O^T:
+ *   o    : [B, H, N, 2d], the attention output (e.g. of diffattn_fwd)
+ *   w_o  : [d_out, H * 2d]; d_out a multiple of 4
+ *   y    : [B, N, d_out] written
+ *   d in {16, 32, 64, 128}; B * N <= 8388480.
+ */
+DIFFATTN_API diffattn_status diffattn_out_proj(const void* o, const void* w_o, int B, int H, int N, int d, int d_out,
+                                  void* y, void* stream);
 
 /* Static English text for a status code (never NULL). */
 DIFFATTN_API const char* diffattn_strerror(diffattn_status status);

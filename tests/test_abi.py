@@ -37,7 +37,7 @@ def test_header_declares_the_abi():
     assert declared_symbols() == sorted([
         "diffattn_abi_version", "diffattn_bwd", "diffattn_bwd_workspace_bytes", "diffattn_decode",
         "diffattn_decode_workspace_bytes", "diffattn_fwd", "diffattn_fwd_fp8qk", "diffattn_fwd_train",
-        "diffattn_lambda", "diffattn_lambda_bwd", "diffattn_quantize_fp8", "diffattn_quantize_fp8_workspace_bytes",
+        "diffattn_in_proj", "diffattn_lambda", "diffattn_lambda_bwd", "diffattn_out_proj", "diffattn_quantize_fp8", "diffattn_quantize_fp8_workspace_bytes",
         "diffattn_strerror"])
 
 
@@ -52,7 +52,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_strerror(L):
-    assert L.diffattn_abi_version() == 3
+    assert L.diffattn_abi_version() == 4
     for code in range(5):
         assert L.diffattn_strerror(code)
     assert L.diffattn_strerror(99) == b"unknown status"
@@ -217,6 +217,31 @@ def test_quantize_fp8_validation(L):
     assert q(A16, 100, A16, None, A16, 4096, None) == b.EINVAL
     assert q(A16, 100, A16, A16, None, 4096, None) == b.EWORKSPACE
     assert q(A16, 1 << 30, A16, A16, A16, 16, None) == b.EWORKSPACE
+
+
+def test_projection_validation(L):
+    ip = lambda B=1, N=8, dm=64, H=2, d=64, ptrs=(A16,) * 7: L.diffattn_in_proj(  # noqa: E731
+        ptrs[0], ptrs[1], B, N, dm, H, d, *ptrs[2:], None)
+    assert ip(d=48) == b.EUNSUPPORTED
+    assert ip(dm=60) == b.EINVAL  # d_model must be a multiple of 8
+    assert ip(H=0) == b.EINVAL
+    assert ip(B=-1) == b.EINVAL
+    assert ip(B=65536, N=129) == b.EINVAL  # more token tiles than one grid dimension holds
+    for i in range(7):
+        p = [A16] * 7
+        p[i] = MIS
+        assert ip(ptrs=p) == b.EINVAL, i
+    assert ip(N=0, ptrs=(None,) * 7) == b.OK
+    op = lambda B=1, H=2, N=8, d=64, dout=64, ptrs=(A16,) * 3: L.diffattn_out_proj(  # noqa: E731
+        ptrs[0], ptrs[1], B, H, N, d, dout, ptrs[2], None)
+    assert op(d=8) == b.EUNSUPPORTED
+    assert op(dout=6) == b.EINVAL  # d_out must be a multiple of 4
+    assert op(H=0) == b.EINVAL
+    for i in range(3):
+        p = [A16] * 3
+        p[i] = None
+        assert op(ptrs=p) == b.EINVAL, i
+    assert op(B=0, ptrs=(None,) * 3) == b.OK
 
 
 def test_lambda_bwd_validation(L):

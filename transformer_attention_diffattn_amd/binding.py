@@ -59,6 +59,10 @@ def lib() -> ctypes.CDLL:
         L.diffattn_quantize_fp8.restype = i
         L.diffattn_fwd_fp8qk.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, vp, f, vp, f, u, vp]
         L.diffattn_fwd_fp8qk.restype = i
+        L.diffattn_in_proj.argtypes = [vp, vp, i, i, i, i, i, vp, vp, vp, vp, vp, vp]
+        L.diffattn_in_proj.restype = i
+        L.diffattn_out_proj.argtypes = [vp, vp, i, i, i, i, i, vp, vp]
+        L.diffattn_out_proj.restype = i
         L.diffattn_abi_version.argtypes = []
         L.diffattn_abi_version.restype = i
         _lib = L
@@ -313,3 +317,41 @@ def fwd_fp8qk(q1, k1, q2, k2, qk_scale, v, lam_t, lambda_init: float, weight=Non
                                     B, H, N, d, _ptr(lam_t), float(lambda_init), _ptr(weight), float(eps),
                                     flags, _stream(q1.device)), "diffattn_fwd_fp8qk")
     return out
+
+
+def in_proj(x, w_qkv, H: int, d: int, outs=None):
+    """x bf16 [B,N,d_model], w_qkv bf16 [3*H*2d, d_model] -> (q1, k1, q2, k2
+    [B,H,N,d], v [B,H,N,2d]), bf16, in the attention's layout."""
+    _dev(x, "x")
+    _dev(w_qkv, "w_qkv")
+    if x.dtype != torch.bfloat16 or w_qkv.dtype != torch.bfloat16 or x.dim() != 3:
+        raise ValueError("x must be bf16 [B,N,d_model] and w_qkv bf16")
+    B, N, dm = x.shape
+    if w_qkv.shape != (3 * H * 2 * d, dm):
+        raise ValueError("w_qkv must be [3*H*2d, d_model]")
+    if outs is None:
+        outs = tuple(torch.empty((B, H, N, d), dtype=torch.bfloat16, device=x.device) for _ in range(4)) + (
+            torch.empty((B, H, N, 2 * d), dtype=torch.bfloat16, device=x.device),)
+    for n, t in zip(("q1", "k1", "q2", "k2", "v"), outs):
+        _dev(t, n)
+    _check(lib().diffattn_in_proj(_ptr(x), _ptr(w_qkv), B, N, dm, H, d, *(_ptr(t) for t in outs),
+                                  _stream(x.device)), "diffattn_in_proj")
+    return outs
+
+
+def out_proj(o, w_o, out=None):
+    """o bf16 [B,H,N,2d], w_o bf16 [d_out, H*2d] -> y bf16 [B,N,d_out]."""
+    _dev(o, "o")
+    _dev(w_o, "w_o")
+    if o.dtype != torch.bfloat16 or w_o.dtype != torch.bfloat16 or o.dim() != 4:
+        raise ValueError("o must be bf16 [B,H,N,2d] and w_o bf16")
+    B, H, N, dv = o.shape
+    if w_o.dim() != 2 or w_o.shape[1] != H * dv:
+        raise ValueError("w_o must be [d_out, H*2d]")
+    if out is None:
+        out = torch.empty((B, N, w_o.shape[0]), dtype=torch.bfloat16, device=o.device)
+    _dev(out, "out")
+    _check(lib().diffattn_out_proj(_ptr(o), _ptr(w_o), B, H, N, dv // 2, w_o.shape[0], _ptr(out),
+                                   _stream(o.device)), "diffattn_out_proj")
+    return out
+

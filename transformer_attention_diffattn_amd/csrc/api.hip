@@ -140,6 +140,67 @@ diffattn_status diffattn_fwd_fp8qk(const void* q1, const void* k1, const void* q
                   nullptr, nullptr, stream, qk_scale);
 }
 
+static int log2_exact(int v) {
+  int l = 0;
+  while ((1 << l) < v) ++l;
+  return (1 << l) == v ? l : -1;
+}
+
+// grid: feature tiles in x, token tiles in y (at most 65535 each, 128 per tile)
+static bool proj_grid_ok(long long M, long long F) {
+  return M <= 65535LL * 128 && F <= 65535LL * 128;
+}
+
+diffattn_status diffattn_in_proj(const void* x, const void* w_qkv, int B, int N, int d_model, int H, int d,
+                                 void* q1, void* k1, void* q2, void* k2, void* v, void* stream) {
+  if (!supported_d(d)) return DIFFATTN_EUNSUPPORTED;
+  if (B < 0 || N < 0 || H < 1 || d_model < 8 || d_model % 8 != 0) return DIFFATTN_EINVAL;
+  const long long M = (long long)B * N, F = 3LL * H * 2 * d;
+  if (!proj_grid_ok(M, F)) return DIFFATTN_EINVAL;
+  if (M == 0) return DIFFATTN_OK;
+  if (!ok_ptr16(x) || !ok_ptr16(w_qkv) || !ok_ptr16(q1) || !ok_ptr16(k1) || !ok_ptr16(q2) || !ok_ptr16(k2) ||
+      !ok_ptr16(v))
+    return DIFFATTN_EINVAL;
+  diffattn::ProjArgs a = {};
+  a.w = w_qkv;
+  a.x = x;
+  a.q1 = q1;
+  a.k1 = k1;
+  a.q2 = q2;
+  a.k2 = k2;
+  a.v = v;
+  a.M = M;
+  a.K = d_model;
+  a.F = (int)F;
+  a.N = N;
+  a.H = H;
+  a.log2_dv = log2_exact(2 * d);
+  hipError_t e = diffattn::launch_proj(0, a, (hipStream_t)stream);
+  return e == hipSuccess ? DIFFATTN_OK : DIFFATTN_EHIP;
+}
+
+diffattn_status diffattn_out_proj(const void* o, const void* w_o, int B, int H, int N, int d, int d_out, void* y,
+                                  void* stream) {
+  if (!supported_d(d)) return DIFFATTN_EUNSUPPORTED;
+  if (B < 0 || N < 0 || H < 1 || d_out < 4 || d_out % 4 != 0) return DIFFATTN_EINVAL;
+  const long long M = (long long)B * N, K = (long long)H * 2 * d;
+  if (!proj_grid_ok(M, d_out) || K > INT32_MAX) return DIFFATTN_EINVAL;
+  if (M == 0) return DIFFATTN_OK;
+  if (!ok_ptr16(o) || !ok_ptr16(w_o) || !ok_ptr16(y)) return DIFFATTN_EINVAL;
+  diffattn::ProjArgs a = {};
+  a.w = w_o;
+  a.x = o;
+  a.y = y;
+  a.M = M;
+  a.K = (int)K;
+  a.F = d_out;
+  a.N = N;
+  a.H = H;
+  a.log2_dv = log2_exact(2 * d);
+  hipError_t e = diffattn::launch_proj(1, a, (hipStream_t)stream);
+  return e == hipSuccess ? DIFFATTN_OK : DIFFATTN_EHIP;
+}
+
 size_t diffattn_quantize_fp8_workspace_bytes(long long n) {
   if (n < 0) return 0;
   return (size_t)diffattn::quant_partial_blocks(n) * sizeof(float);

@@ -73,6 +73,25 @@ struct BwdArgs {
   float c;              // log2(e) / sqrt(d)
 };
 
+struct ProjArgs {
+  const void* w;    // bf16 [F][K] (linear-layer layout: out x in)
+  const void* x;    // in-projection: bf16 [M][K]; out-projection: bf16 [B][H][N][2d]
+  void* q1;         // in-projection outputs: bf16 [B][H][N][d] (x4) and [B][H][N][2d]
+  void* k1;
+  void* q2;
+  void* k2;
+  void* v;
+  void* y;          // out-projection output: bf16 [M][F]
+  long long M;      // tokens, B * N
+  int K;            // reduction length (multiple of 8)
+  int F;            // output features (multiple of 4)
+  int N, H;
+  int log2_dv;      // log2(2d)
+};
+
+// mode 0: in-projection, 1: out-projection
+hipError_t launch_proj(int mode, const ProjArgs& a, hipStream_t stream);
+
 // Query rows and threads per workgroup of the prefill kernels.
 int prefill_block_rows(bool bf16, int d);
 int prefill_block_threads(bool bf16, int d);

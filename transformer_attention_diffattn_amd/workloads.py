@@ -126,6 +126,24 @@ def prefill_inputs(B, H, N, d, dtype="bf16", seed=0, *, lambda_init=0.8, lam_std
     )
 
 
+def projection_inputs(B, N, d_model, H, d, seed=0, *, d_out=None, device="cpu"):
+    """Seeded inputs of the projections either side of the attention (bf16):
+    x [B, N, d_model] ~ N(0, 1); w_qkv [3*H*2d, d_model] and
+    w_o [d_out, H*2d] ~ N(0, 1/fan_in) (fan-in scaled, as a linear layer's
+    initialisation); o [B, H, N, 2d] ~ N(0, 1) stands in for the attention
+    output."""
+    g = _gen(seed, device)
+    width = H * 2 * d
+    d_out = d_model if d_out is None else d_out
+    x = torch.randn((B, N, d_model), generator=g, device=device)
+    w_qkv = torch.randn((3 * width, d_model), generator=g, device=device) / math.sqrt(d_model)
+    w_o = torch.randn((d_out, width), generator=g, device=device) / math.sqrt(width)
+    o = torch.randn((B, H, N, 2 * d), generator=g, device=device)
+    bf = torch.bfloat16
+    return dict(x=x.to(bf).contiguous(), w_qkv=w_qkv.to(bf).contiguous(), w_o=w_o.to(bf).contiguous(),
+                o=o.to(bf).contiguous())
+
+
 def decode_inputs(B, H, L, d, dtype="bf16", seed=0, *, lambda_init=0.8, lam_std=0.1,
                   cache_len=None, device="cpu", eps=1e-5):
     """Seeded decode inputs: one query token per sequence and a KV cache of
