@@ -169,6 +169,50 @@ def reference_gemm(torch, dev, n: int = 8192, seconds: float = 0.5):
     return 2.0 * n ** 3 / (ms * 1e-3) / 1e12
 
 
+def proj_leg(args, stream, torch, da, W):
+    """The in- and out-projections of the 1.4B-scale layer (4 x 2048 tokens,
+    d_model 2048, 16 heads of 2d = 128), each replayed from a graph of 10
+    calls, with the vendor bf16 GEMM of the same shapes (plain products, no
+    head split) timed beside them for context."""
+    B, N, dm, H, d = 4, 2048, 2048, 16, 64
+    dev = torch.device("cuda:0")
+    x = W.projection_inputs(B, N, dm, H, d, seed=20266, device=dev)
+    outs = da.in_proj(x["x"], x["w_qkv"], H, d)
+    y = da.out_proj(x["o"], x["w_o"])
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in outs] + [y.clone()]
+    R = 10
+    steps = max(R, args.proj_steps // R * R)
+    x2 = x["x"].reshape(B * N, dm)
+    wq_t = x["w_qkv"].t().contiguous()
+    o2 = x["o"].transpose(1, 2).reshape(B * N, H * 2 * d).contiguous()
+    wo_t = x["w_o"].t().contiguous()
+    ms = {}
+    for name, fn in (("in", lambda: da.in_proj(x["x"], x["w_qkv"], H, d, outs=outs)),
+                     ("out", lambda: da.out_proj(x["o"], x["w_o"], out=y)),
+                     ("vendor_in", lambda: torch.matmul(x2, wq_t)),
+                     ("vendor_out", lambda: torch.matmul(o2, wo_t))):
+        g = _graph(lambda fn=fn: [fn() for _ in range(R)], torch)
+        _prewarm(g.replay, min(0.3, args.prewarm_s), torch)
+        ms[name] = _timed(g.replay, steps // R, stream, torch) / steps
+    for a, b in zip(list(outs) + [y], eager):
+        if not torch.equal(a, b):
+            raise RuntimeError("graph replay of a projection differs from the eager call")
+    M = B * N
+    f_in, f_out = 2.0 * M * dm * 3 * H * 2 * d, 2.0 * M * H * 2 * d * dm
+    t_in, t_out = f_in / (ms["in"] * 1e-3) / 1e12, f_out / (ms["out"] * 1e-3) / 1e12
+    return {
+        "shape": {"tokens": M, "d_model": dm, "H": H, "d": d},
+        "in_proj": {"ms": round(ms["in"], 4), "tflops": round(t_in, 1),
+                    "vendor_gemm_tflops": round(f_in / (ms["vendor_in"] * 1e-3) / 1e12, 1)},
+        "out_proj": {"ms": round(ms["out"], 4), "tflops": round(t_out, 1),
+                     "vendor_gemm_tflops": round(f_out / (ms["vendor_out"] * 1e-3) / 1e12, 1)},
+        "roofline": {"bound": "mfma", "kernel": "proj_kernel<in-projection>", "achieved": round(t_in, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(t_in / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+    }
+
+
 def backward_leg(x, w, args, stream, torch, da):
     """diffattn_fwd_train and diffattn_bwd on the same workload, each replayed
     from a HIP graph (checked equal to the eager call).  The backward is priced
@@ -333,6 +377,8 @@ def main():
     ap.add_argument("--no-bwd", action="store_true", help="skip the training (backward) leg")
     ap.add_argument("--bwd-steps", type=int, default=40)
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 query/key prefill leg")
+    ap.add_argument("--no-proj", action="store_true", help="skip the projection leg")
+    ap.add_argument("--proj-steps", type=int, default=40)
     ap.add_argument("--fp8-steps", type=int, default=40)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of CPU oracle time")
@@ -476,6 +522,14 @@ def main():
         except Exception as e:  # noqa: BLE001
             print(f"fp8 leg failed: {e!r}", file=sys.stderr, flush=True)
             res["fp8_qk"] = {"error": repr(e)}
+
+    # ---------------- projections either side of the attention
+    if not args.no_proj:
+        try:
+            res["projections"] = proj_leg(args, stream, torch, da, W)
+        except Exception as e:  # noqa: BLE001
+            print(f"projection leg failed: {e!r}", file=sys.stderr, flush=True)
+            res["projections"] = {"error": repr(e)}
 
     if not args.no_ref_gemm:
         g = reference_gemm(torch, dev)

@@ -19,9 +19,9 @@
 //                    h*2d + c), y = X W_O^T written row-major [B*N, d_out].
 //
 // Workgroup: 4 waves as 2 x 2, a 128-feature x 128-token tile; each wave
-// owns 64 x 64 (4 x 4 MFMA blocks) and streams its fragments straight from
-// global memory (the four waves' overlapping rows meet in the L1/L2), the
-// next reduction step's loads issued before the current step's products.
+// owns 64 x 64 (4 x 4 MFMA blocks).  Operand tiles are staged in LDS, 64
+// reduction elements per step, the next step's global loads in flight while
+// the current step's products run.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -45,49 +45,63 @@ __global__ __launch_bounds__(256, 2) void proj_kernel(ProjArgs a) {
   const int K = a.K, F = a.F, M = a.M, N = a.N, H = a.H;
   const int l2dv = a.log2_dv;  // 2d = 1 << l2dv (out-projection reads; in-projection writes)
 
-  const uint16_t* wrow[4];
+  // The workgroup's operand tiles pass through LDS, 64 reduction elements
+  // (128 bytes per row) at a time, double-buffered: 128 feature rows of W
+  // and 128 token rows of X, each row's eight 16-byte chunks XOR-swizzled by
+  // (row mod 8) so that the 16 rows one fragment read touches spread over
+  // all banks.  Thread t loads chunks t + 256u (u < 4) of each tile: eight
+  // consecutive threads cover one row's 128 bytes.
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][kProjTile * 64];  // [buffer][W, X][row*64 + k]
+  const int tid = threadIdx.x;
+  const int wf0 = blockIdx.x * kProjTile, wm0 = blockIdx.y * kProjTile;  // workgroup's first feature / token
+  const uint16_t* wsrc[4];
+  const uint16_t* xsrc[4];
+  int lrow[4], lchk[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) wrow[i] = (const uint16_t*)a.w + (size_t)min(n0 + 16 * i + lr, F - 1) * K;
-  // token rows (b, t) of this lane's four tokens; the x rows (in-projection)
-  // or head 0 of the token (out-projection; head h lies h*N*2d further)
-  int tb[4], tt[4];
-  const uint16_t* xrow[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int m = min(m0 + 16 * j + lr, M - 1);
-    tb[j] = m / N;
-    tt[j] = m - tb[j] * N;
-    if (MODE == 0)
-      xrow[j] = (const uint16_t*)a.x + (size_t)m * K;
-    else
-      xrow[j] = (const uint16_t*)a.x + (((size_t)tb[j] * H * N + (size_t)tt[j]) << l2dv);
+  for (int u = 0; u < 4; ++u) {
+    const int q = tid + 256 * u;
+    const int r = q >> 3, c = q & 7;
+    lrow[u] = r;
+    lchk[u] = c;
+    wsrc[u] = (const uint16_t*)a.w + (size_t)min(wf0 + r, F - 1) * K;
+    const int m = min(wm0 + r, M - 1);
+    if (MODE == 0) {
+      xsrc[u] = (const uint16_t*)a.x + (size_t)m * K;
+    } else {
+      const int b = m / N, t = m - b * N;
+      xsrc[u] = (const uint16_t*)a.x + (((size_t)b * H * N + (size_t)t) << l2dv);
+    }
   }
   const size_t head_stride = (size_t)N << l2dv;  // out-projection: elements between heads
-
-  // fragments of reduction step k0; past K they are zero (the address is
-  // clamped to the last chunk, so every load stays inside its row)
-  auto load = [&](int k0, bf16x8 (&af)[4], bf16x8 (&bfr)[4]) {
-    const int kk0 = k0 + 8 * lg;
-    const bool ok = kk0 < K;
-    const int kk = min(kk0, K - 8);
+  u32x4 stw[4], stx[4];
+  // global -> registers: chunk (row, c) of step k0; zero past K (address clamped)
+  auto fetch = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const u32x4 t = ld16(wrow[i] + kk);
-      af[i] = as_bf16x8(ok ? t : zero_u32x4());
-    }
-    size_t off = (size_t)kk;
-    if (MODE == 1) off = (size_t)(kk >> l2dv) * head_stride + (size_t)(kk & ((1 << l2dv) - 1));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const u32x4 t = ld16(xrow[j] + off);
-      bfr[j] = as_bf16x8(ok ? t : zero_u32x4());
+    for (int u = 0; u < 4; ++u) {
+      const int kk0 = k0 + 8 * lchk[u];
+      const bool ok = kk0 < K;
+      const int kk = min(kk0, K - 8);
+      const u32x4 tw = ld16(wsrc[u] + kk);
+      size_t off = (size_t)kk;
+      if (MODE == 1) off = (size_t)(kk >> l2dv) * head_stride + (size_t)(kk & ((1 << l2dv) - 1));
+      const u32x4 tx = ld16(xsrc[u] + off);
+      stw[u] = ok ? tw : zero_u32x4();
+      stx[u] = ok ? tx : zero_u32x4();
     }
   };
-  auto mma = [&](const bf16x8 (&af)[4], const bf16x8 (&bfr)[4], f32x4 (&acc)[4][4]) {
+  auto stash = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32_bf16(af[i], bfr[j], acc[i][j]);
+    for (int u = 0; u < 4; ++u) {
+      const int e = lrow[u] * 64 + 8 * (lchk[u] ^ (lrow[u] & 7));
+      *reinterpret_cast<u32x4*>(&lds[buf][0][e]) = stw[u];
+      *reinterpret_cast<u32x4*>(&lds[buf][1][e]) = stx[u];
+    }
+  };
+  // fragments of half s (k 32s..32s+31) of the staged step: row 16i + lr of
+  // the wave's 64 rows, chunk 4s + lg
+  const int wrow0 = (wave & 1) * 64, xrow0 = (wave >> 1) * 64;
+  auto frag = [&](const uint16_t* t, int row, int s) {
+    return as_bf16x8(*reinterpret_cast<const u32x4*>(t + row * 64 + 8 * ((4 * s + lg) ^ (row & 7))));
   };
 
   f32x4 acc[4][4];
@@ -96,17 +110,37 @@ __global__ __launch_bounds__(256, 2) void proj_kernel(ProjArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = zero_f32x4();
 
-  // two register buffers, the loop unrolled by two so that both are named
-  // at compile time; each step's loads are issued before the previous
-  // step's products
-  bf16x8 a0[4], b0[4], a1[4], b1[4];
-  load(0, a0, b0);
-  for (int k0 = 0; k0 < K; k0 += 64) {
-    load(k0 + 32, a1, b1);
-    mma(a0, b0, acc);
-    if (k0 + 32 >= K) break;
-    load(k0 + 64, a0, b0);
-    mma(a1, b1, acc);
+  const int nk = (K + 63) / 64;
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  for (int ks = 0; ks < nk; ++ks) {
+    const int buf = ks & 1;
+    if (ks + 1 < nk) fetch(64 * (ks + 1));
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      bf16x8 af[4], bfr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[i] = frag(lds[buf][0], wrow0 + 16 * i + lr, s);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bfr[j] = frag(lds[buf][1], xrow0 + 16 * j + lr, s);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32_bf16(af[i], bfr[j], acc[i][j]);
+    }
+    // the other buffer was last read in the previous step, before its barrier
+    if (ks + 1 < nk) stash(buf ^ 1);
+    __syncthreads();
+  }
+
+  // token rows (b, t) of this lane's four tokens, for the epilogue
+  int tb[4], tt[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int m = min(m0 + 16 * j + lr, M - 1);
+    tb[j] = m / N;
+    tt[j] = m - tb[j] * N;
   }
 
   // lane: token m0 + 16j + lr, features n0 + 16i + 4lg .. +3 (8 bytes of bf16)
