@@ -209,7 +209,7 @@ def proj_leg(args, stream, torch, da, W):
                      "vendor_gemm_tflops": round(f_out / (ms["vendor_out"] * 1e-3) / 1e12, 1)},
         "roofline": {"bound": "mfma", "kernel": "proj_kernel<in-projection>", "achieved": round(t_in, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(t_in / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": _traffic("proj_in_layer1p4b", "proj.hip"), "algorithmic_bytes": 159383552},
     }
 
 

@@ -40,8 +40,22 @@ __global__ __launch_bounds__(256, 2) void proj_kernel(ProjArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int lr = lane & 15, lg = lane >> 4;
-  const int n0 = blockIdx.x * kProjTile + (wave & 1) * 64;  // output features
-  const int m0 = blockIdx.y * kProjTile + (wave >> 1) * 64;  // tokens (M < 2^23)
+  // Tile order.  Workgroups are dealt to the 8 XCDs round-robin by launch
+  // index, each XCD with its own L2: XCD x takes the x-th eighth of a
+  // sequence in which GM token tiles run with all feature tiles before the
+  // next GM, so each XCD keeps a few token slabs resident while it streams
+  // the weight rows (a bijection of the tile grid; plain order if the tile
+  // count is not a multiple of 8).
+  constexpr int GM = 8;
+  const int nF = gridDim.x, nMt = gridDim.y, total = nF * nMt;
+  const int L = blockIdx.x + nF * blockIdx.y;
+  const int seq = (total % 8 == 0) ? (L % 8) * (total / 8) + L / 8 : L;
+  const int grp = seq / (GM * nF), first_m = grp * GM;
+  const int gm = min(nMt - first_m, GM);
+  const int rem = seq - grp * GM * nF;
+  const int tile_m = first_m + rem % gm, tile_f = rem / gm;
+  const int n0 = tile_f * kProjTile + (wave & 1) * 64;  // output features
+  const int m0 = tile_m * kProjTile + (wave >> 1) * 64;  // tokens (M < 2^23)
   const int K = a.K, F = a.F, M = a.M, N = a.N, H = a.H;
   const int l2dv = a.log2_dv;  // 2d = 1 << l2dv (out-projection reads; in-projection writes)
 
@@ -53,7 +67,7 @@ __global__ __launch_bounds__(256, 2) void proj_kernel(ProjArgs a) {
   // consecutive threads cover one row's 128 bytes.
   __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][kProjTile * 64];  // [buffer][W, X][row*64 + k]
   const int tid = threadIdx.x;
-  const int wf0 = blockIdx.x * kProjTile, wm0 = blockIdx.y * kProjTile;  // workgroup's first feature / token
+  const int wf0 = tile_f * kProjTile, wm0 = tile_m * kProjTile;  // workgroup's first feature / token
   const uint16_t* wsrc[4];
   const uint16_t* xsrc[4];
   int lrow[4], lchk[4];
