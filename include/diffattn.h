@@ -205,7 +205,7 @@ DIFFATTN_API diffattn_status diffattn_lambda_bwd(const float* lq1, const float* 
  * (bias 7, no infinities, largest finite value 448).
  *
  * diffattn_quantize_fp8_workspace_bytes -- device scratch bytes that
- * diffattn_quantize_fp8 needs for n values (at most 4096; 0 for n < 0).
+ * diffattn_quantize_fp8 needs for n values (at most 1024; 0 for n < 0).
  */
 DIFFATTN_API size_t diffattn_quantize_fp8_workspace_bytes(long long n);
 

@@ -22,7 +22,8 @@ namespace diffattn {
 namespace {
 
 constexpr int kQuantThreads = 256;
-constexpr int kMaxPartials = 1024;
+constexpr int kMaxPartials = 256;   // pass 1 workgroups: few partials for every pass-2 workgroup to reduce
+constexpr int kMaxEncodeGroups = 2048;
 
 // fp32 -> e4m3 code: round to nearest even, saturating at 448.
 //   |y| >= 448          -> 0x7E
@@ -65,6 +66,7 @@ __global__ __launch_bounds__(kQuantThreads) void amax_partial_kernel(const uint1
   __shared__ uint32_t sh[kQuantThreads / 64];
   const long long chunks = n / 8;
   uint32_t m = 0;  // bf16 magnitude bits
+#pragma unroll 4
   for (long long i = (long long)blockIdx.x * kQuantThreads + threadIdx.x; i < chunks;
        i += (long long)gridDim.x * kQuantThreads) {
     const u32x4 w = ld16(x + 8 * i);
@@ -93,6 +95,7 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(const uint16_t*
   const float inv = amax > 0.f ? 448.0f / amax : 1.0f;
   if (blockIdx.x == 0 && threadIdx.x == 0) scale[0] = amax > 0.f ? amax / 448.0f : 1.0f;
   const long long chunks = n / 8;
+#pragma unroll 2
   for (long long i = (long long)blockIdx.x * kQuantThreads + threadIdx.x; i < chunks;
        i += (long long)gridDim.x * kQuantThreads) {
     const u32x4 w = ld16(x + 8 * i);
@@ -120,7 +123,7 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(const uint16_t*
 
 int quant_partial_blocks(long long n) {
   const long long chunks = (n + 7) / 8;
-  const long long b = (chunks + 4 * kQuantThreads - 1) / (4 * kQuantThreads);
+  const long long b = (chunks + 8 * kQuantThreads - 1) / (8 * kQuantThreads);
   return (int)(b < 1 ? 1 : (b > kMaxPartials ? kMaxPartials : b));
 }
 
@@ -129,7 +132,7 @@ hipError_t launch_quantize_fp8(const void* x, long long n, float* partial, uint8
   const int P = quant_partial_blocks(n);
   const long long chunks = n / 8;
   long long g = (chunks + kQuantThreads - 1) / kQuantThreads;
-  g = g < 1 ? 1 : (g > 8192 ? 8192 : g);
+  g = g < 1 ? 1 : (g > kMaxEncodeGroups ? kMaxEncodeGroups : g);
   hipLaunchKernelGGL(amax_partial_kernel, dim3(P), dim3(kQuantThreads), 0, stream, (const uint16_t*)x, n, partial);
   hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)g), dim3(kQuantThreads), 0, stream, (const uint16_t*)x, n,
                      partial, P, codes, scale);
