@@ -228,6 +228,35 @@ def test_fp8qk_full_size_3b_layer_sampled(dev):
     assert worst <= 2e-2
 
 
+def test_fp8qk_longctx_64k_sampled(dev):
+    # 64K tokens, 12 heads, d = 128, with the planted needles: sampled rows
+    # (needle offsets, first and last rows) of two heads against the oracle
+    # on the dequantised inputs, each row with its full causal prefix
+    name = "longctx_bf16_b1h12n65536d128"
+    x = W.workload_inputs(name, device=dev)
+    codes, scales = {}, torch.empty(4, dtype=torch.float32, device=dev)
+    for i, k in enumerate(("q1", "k1", "q2", "k2")):
+        codes[k], _ = da.quantize_fp8(x[k], scale=scales[i:i + 1])
+    lam_t = da.lam(x["lq1"], x["lk1"], x["lq2"], x["lk2"], x["lambda_init"])
+    out = da.fwd_fp8qk(codes["q1"], codes["k1"], codes["q2"], codes["k2"], scales, x["v"], lam_t,
+                       x["lambda_init"], eps=x["eps"], causal=True)
+    torch.cuda.synchronize()
+    lam = float(lam_t.item())
+    sc = scales.cpu().numpy()
+    N = x["q1"].shape[2]
+    rows = np.array([0, 6, 7, 8, 311, 312, 5003, 40009, 40010, N - 1])
+    worst = 0.0
+    for h in (0, 11):
+        deq = [F.dequantize(codes[k][0, h].cpu().numpy(), sc[i]) for i, k in enumerate(("q1", "k1", "q2", "k2"))]
+        ref = O.forward_rows(deq[0], deq[1], deq[2], deq[3], x["v"][0, h].cpu(), rows, lam, x["lambda_init"],
+                             eps=x["eps"], causal=True)
+        got = out[0, h][torch.from_numpy(rows).to(dev)].float().cpu().numpy()
+        assert np.all(np.isfinite(got))
+        worst = max(worst, float(np.max(np.abs(got - ref))))
+    print(f"{name} fp8qk: sampled max|err| = {worst:.3e}", flush=True)
+    assert worst <= 2e-2
+
+
 def test_fp8qk_deterministic(dev):
     x = W.prefill_inputs(1, 2, 700, D, "bf16", seed=71)
     codes, scales, _ = _oracle_quant(x)

@@ -85,6 +85,24 @@ def test_projections_full_size_1p4b_layer_sampled(dev):
            P.out_projection(_abs(os_), _abs(x["w_o"].cpu())), H * 2 * d)
 
 
+def test_projections_full_size_3b_layer_sampled(dev):
+    # 2 x 4096 tokens, d_model 3072, 12 heads of 2d = 256 (d = 128)
+    B, N, dm, H, d = 2, 4096, 3072, 12, 128
+    x = W.projection_inputs(B, N, dm, H, d, seed=20267, device=dev)
+    outs = da.in_proj(x["x"], x["w_qkv"], H, d)
+    y = da.out_proj(x["o"], x["w_o"])
+    torch.cuda.synchronize()
+    rows = np.array([0, 127, 128, 2049, N - 1])
+    xs = x["x"][:, rows].cpu()
+    ref = P.in_projection(xs, x["w_qkv"].cpu(), H, d)
+    mag = P.in_projection(_abs(xs), _abs(x["w_qkv"].cpu()), H, d)
+    for g, r, m in zip(outs, ref, mag):
+        _check(g[:, :, rows], r, m, dm)
+    os_ = x["o"][:, :, rows].cpu()
+    _check(y[:, rows], P.out_projection(os_, x["w_o"].cpu()),
+           P.out_projection(_abs(os_), _abs(x["w_o"].cpu())), H * 2 * d)
+
+
 def test_layer_chain_runs_on_device_layouts(dev):
     # in_proj -> diffattn_fwd -> out_proj with no copies between them: the
     # projection outputs are the attention's inputs as they stand
