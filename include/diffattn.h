@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define DIFFATTN_ABI_VERSION 4
+#define DIFFATTN_ABI_VERSION 5
 
 #if defined(__GNUC__) || defined(__clang__)
 #define DIFFATTN_API __attribute__((visibility("default")))
@@ -223,6 +223,18 @@ DIFFATTN_API size_t diffattn_quantize_fp8_workspace_bytes(long long n);
  */
 DIFFATTN_API diffattn_status diffattn_quantize_fp8(const void* x, long long n, void* codes, float* scale,
                                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * diffattn_quantize_fp8_batch -- diffattn_quantize_fp8 of count (1..4)
+ * tensors of n values each in one pair of launches: x[t] -> codes[t] and
+ * scales[t].  x and codes are HOST arrays of count device pointers (each
+ * 16-byte aligned); scales is device fp32 [count]; the workspace holds at
+ * least count * diffattn_quantize_fp8_workspace_bytes(n) bytes.  Results are
+ * those of count separate diffattn_quantize_fp8 calls.
+ */
+DIFFATTN_API diffattn_status diffattn_quantize_fp8_batch(int count, const void* const* x, long long n,
+                                            void* const* codes, float* scales, void* workspace,
+                                            size_t workspace_bytes, void* stream);
 
 /*
  * diffattn_fwd_fp8qk -- the prefill of diffattn_fwd (Eq. 1 then Eq. 3) with

@@ -37,7 +37,7 @@ def test_header_declares_the_abi():
     assert declared_symbols() == sorted([
         "diffattn_abi_version", "diffattn_bwd", "diffattn_bwd_workspace_bytes", "diffattn_decode",
         "diffattn_decode_workspace_bytes", "diffattn_fwd", "diffattn_fwd_fp8qk", "diffattn_fwd_train",
-        "diffattn_in_proj", "diffattn_lambda", "diffattn_lambda_bwd", "diffattn_out_proj", "diffattn_quantize_fp8", "diffattn_quantize_fp8_workspace_bytes",
+        "diffattn_in_proj", "diffattn_lambda", "diffattn_lambda_bwd", "diffattn_out_proj", "diffattn_quantize_fp8", "diffattn_quantize_fp8_batch", "diffattn_quantize_fp8_workspace_bytes",
         "diffattn_strerror"])
 
 
@@ -52,7 +52,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_strerror(L):
-    assert L.diffattn_abi_version() == 4
+    assert L.diffattn_abi_version() == 5
     for code in range(5):
         assert L.diffattn_strerror(code)
     assert L.diffattn_strerror(99) == b"unknown status"
@@ -217,6 +217,23 @@ def test_quantize_fp8_validation(L):
     assert q(A16, 100, A16, None, A16, 4096, None) == b.EINVAL
     assert q(A16, 100, A16, A16, None, 4096, None) == b.EWORKSPACE
     assert q(A16, 1 << 30, A16, A16, A16, 16, None) == b.EWORKSPACE
+
+
+def test_quantize_fp8_batch_validation(L):
+    import ctypes
+
+    arr = lambda *p: (ctypes.c_void_p * len(p))(*p)  # noqa: E731
+    qb = L.diffattn_quantize_fp8_batch
+    four = arr(A16, A16, A16, A16)
+    assert qb(0, four, 100, four, A16, A16, 4096, None) == b.EINVAL
+    assert qb(5, arr(*([A16] * 5)), 100, arr(*([A16] * 5)), A16, A16, 4096, None) == b.EINVAL
+    assert qb(2, None, 100, four, A16, A16, 4096, None) == b.EINVAL
+    assert qb(2, arr(A16, MIS), 100, four, A16, A16, 4096, None) == b.EINVAL
+    assert qb(2, four, 100, arr(None, A16), A16, A16, 4096, None) == b.EINVAL
+    assert qb(2, four, 100, four, None, A16, 4096, None) == b.EINVAL
+    assert qb(2, four, 100, four, A16, A16, 4, None) == b.EWORKSPACE  # two tensors need 8 bytes
+    assert qb(2, four, -1, four, A16, A16, 4096, None) == b.EINVAL
+    assert qb(2, four, 0, four, A16, A16, 4096, None) == b.OK
 
 
 def test_projection_validation(L):

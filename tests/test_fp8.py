@@ -120,6 +120,18 @@ def test_quantize_special_values(dev, kind):
     assert scale.item() == float(ref_s)
 
 
+@pytest.mark.parametrize("count,n", [(1, 1000), (2, 7), (4, 4099), (4, 2 * 12 * 4096 * D)])
+def test_quantize_batch_equals_oracle(dev, count, n):
+    print(f"case quantize batch count={count} n={n}", flush=True)
+    g = torch.Generator().manual_seed(7000 + n + count)
+    xs = [(torch.randn(n, generator=g) * (0.5 + t)).to(torch.bfloat16) for t in range(count)]
+    codes, scales = da.quantize_fp8_batch([x.to(dev) for x in xs])
+    for t in range(count):
+        ref_c, ref_s = F.quantize(xs[t].float().numpy())
+        assert np.array_equal(codes[t].cpu().numpy(), ref_c), t
+        assert scales[t].item() == float(ref_s), t
+
+
 def test_quantize_full_size_3b_layer(dev):
     # every query/key tensor of the 3B-layer prefill (2 x 12 x 4096 x 128)
     x = W.workload_inputs("layer3b_bf16_b2h12n4096d128", device=dev)

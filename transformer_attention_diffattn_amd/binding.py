@@ -57,6 +57,8 @@ def lib() -> ctypes.CDLL:
         L.diffattn_quantize_fp8_workspace_bytes.restype = sz
         L.diffattn_quantize_fp8.argtypes = [vp, ctypes.c_longlong, vp, vp, vp, sz, vp]
         L.diffattn_quantize_fp8.restype = i
+        L.diffattn_quantize_fp8_batch.argtypes = [i, vp, ctypes.c_longlong, vp, vp, vp, sz, vp]
+        L.diffattn_quantize_fp8_batch.restype = i
         L.diffattn_fwd_fp8qk.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, vp, f, vp, f, u, vp]
         L.diffattn_fwd_fp8qk.restype = i
         L.diffattn_in_proj.argtypes = [vp, vp, i, i, i, i, i, vp, vp, vp, vp, vp, vp]
@@ -283,6 +285,40 @@ def quantize_fp8(x, codes=None, scale=None, workspace=None):
                                        workspace.numel() * workspace.element_size(), _stream(x.device)),
            "diffattn_quantize_fp8")
     return codes, scale
+
+
+def quantize_fp8_batch(xs, codes=None, scales=None, workspace=None):
+    """diffattn_quantize_fp8 of 1..4 bf16 tensors of equal size in one pair of
+    launches: returns (list of uint8 codes, scales fp32 [count])."""
+    count = len(xs)
+    if not 1 <= count <= 4:
+        raise ValueError("one to four tensors")
+    for k, x in enumerate(xs):
+        _dev(x, f"x[{k}]")
+        if x.dtype != torch.bfloat16 or x.numel() != xs[0].numel():
+            raise ValueError("tensors must be bf16 with equal element counts")
+    n = xs[0].numel()
+    dev = xs[0].device
+    if codes is None:
+        codes = [torch.empty(x.shape, dtype=torch.uint8, device=dev) for x in xs]
+    for k, c in enumerate(codes):
+        _dev(c, f"codes[{k}]")
+        if c.dtype != torch.uint8 or c.numel() != n:
+            raise ValueError("codes must be uint8 with x's element count")
+    if scales is None:
+        scales = torch.empty(count, dtype=torch.float32, device=dev)
+    _dev(scales, "scales")
+    if scales.dtype != torch.float32 or scales.numel() != count:
+        raise ValueError("scales must be fp32 [count]")
+    need = count * quantize_fp8_workspace_bytes(n)
+    if workspace is None:
+        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=dev)
+    xp = (ctypes.c_void_p * count)(*(x.data_ptr() for x in xs))
+    cp = (ctypes.c_void_p * count)(*(c.data_ptr() for c in codes))
+    _check(lib().diffattn_quantize_fp8_batch(count, xp, n, cp, _ptr(scales), _ptr(workspace),
+                                             workspace.numel() * workspace.element_size(), _stream(dev)),
+           "diffattn_quantize_fp8_batch")
+    return codes, scales
 
 
 def fwd_fp8qk(q1, k1, q2, k2, qk_scale, v, lam_t, lambda_init: float, weight=None, eps: float = 1e-5,

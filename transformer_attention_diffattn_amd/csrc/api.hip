@@ -213,7 +213,23 @@ diffattn_status diffattn_quantize_fp8(const void* x, long long n, void* codes, f
   if (!ok_ptr16(x) || !ok_ptr16(codes) || !ok_ptr4(scale)) return DIFFATTN_EINVAL;
   if (workspace == nullptr || !aligned(workspace, 4) || workspace_bytes < diffattn_quantize_fp8_workspace_bytes(n))
     return DIFFATTN_EWORKSPACE;
-  hipError_t e = diffattn::launch_quantize_fp8(x, n, (float*)workspace, (uint8_t*)codes, scale, (hipStream_t)stream);
+  const void* xs[1] = {x};
+  void* cs[1] = {codes};
+  hipError_t e = diffattn::launch_quantize_fp8(1, xs, n, (float*)workspace, cs, scale, (hipStream_t)stream);
+  return e == hipSuccess ? DIFFATTN_OK : DIFFATTN_EHIP;
+}
+
+diffattn_status diffattn_quantize_fp8_batch(int count, const void* const* x, long long n, void* const* codes,
+                                            float* scales, void* workspace, size_t workspace_bytes, void* stream) {
+  if (count < 1 || count > diffattn::kQuantBatch || x == nullptr || codes == nullptr || n < 0) return DIFFATTN_EINVAL;
+  if (n == 0) return DIFFATTN_OK;
+  for (int t = 0; t < count; ++t)
+    if (!ok_ptr16(x[t]) || !ok_ptr16(codes[t])) return DIFFATTN_EINVAL;
+  if (!ok_ptr4(scales)) return DIFFATTN_EINVAL;
+  if (workspace == nullptr || !aligned(workspace, 4) ||
+      workspace_bytes < (size_t)count * diffattn_quantize_fp8_workspace_bytes(n))
+    return DIFFATTN_EWORKSPACE;
+  hipError_t e = diffattn::launch_quantize_fp8(count, x, n, (float*)workspace, codes, scales, (hipStream_t)stream);
   return e == hipSuccess ? DIFFATTN_OK : DIFFATTN_EHIP;
 }
 

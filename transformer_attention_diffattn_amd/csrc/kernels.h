@@ -104,11 +104,22 @@ hipError_t launch_prefill(bool bf16, int d, bool causal, bool norm, const Prefil
 // d = 128, e4m3 q1/k1/q2/k2 (a.qk_scale set), bf16 v and output
 hipError_t launch_prefill_fp8qk(bool causal, bool norm, const PrefillArgs& a, hipStream_t stream);
 
-// Per-tensor absmax e4m3 quantisation of n bf16 values: partial maxima of
-// quant_partial_blocks(n) workgroups, then the scale and the codes.
+// Per-tensor absmax e4m3 quantisation of `count` (1..kQuantBatch) bf16
+// tensors of n values each: partial maxima of quant_partial_blocks(n)
+// workgroups per tensor (partial: [count][P]), then each tensor's scale
+// (scales[t]) and codes.
+constexpr int kQuantBatch = 4;
+struct QuantBatch {
+  const uint16_t* x[kQuantBatch];
+  uint8_t* codes[kQuantBatch];
+  float* scale;
+  float* partial;
+  long long n;
+  int P;
+};
 int quant_partial_blocks(long long n);
-hipError_t launch_quantize_fp8(const void* x, long long n, float* partial, uint8_t* codes, float* scale,
-                               hipStream_t stream);
+hipError_t launch_quantize_fp8(int count, const void* const* x, long long n, float* partial, void* const* codes,
+                               float* scales, hipStream_t stream);
 
 // Split plan for decode: number of splits and keys per split.
 void decode_plan(int B, int H, int L, int d, int* S, int* chunk);

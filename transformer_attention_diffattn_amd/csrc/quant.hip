@@ -59,11 +59,15 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t x, uint32_t* sh) {
   return r;
 }
 
-// Pass 1: partial[blockIdx.x] = max |x| over this workgroup's 8-value chunks
-// (and, for workgroup 0, the n % 8 values after the last whole chunk).
-__global__ __launch_bounds__(kQuantThreads) void amax_partial_kernel(const uint16_t* __restrict__ x, long long n,
-                                                                     float* __restrict__ partial) {
+// Both passes take up to kQuantBatch tensors of n values at once, one per
+// blockIdx.y: the same two launches then serve all of them.
+// Pass 1: partial[t][blockIdx.x] = max |x_t| over this workgroup's 8-value
+// chunks (and, for workgroup 0, the n % 8 values after the last whole chunk).
+__global__ __launch_bounds__(kQuantThreads) void amax_partial_kernel(QuantBatch q) {
   __shared__ uint32_t sh[kQuantThreads / 64];
+  const uint16_t* __restrict__ x = q.x[blockIdx.y];
+  float* __restrict__ partial = q.partial + (size_t)blockIdx.y * q.P;
+  const long long n = q.n;
   const long long chunks = n / 8;
   uint32_t m = 0;  // bf16 magnitude bits
 #pragma unroll 4
@@ -83,11 +87,14 @@ __global__ __launch_bounds__(kQuantThreads) void amax_partial_kernel(const uint1
 
 // Pass 2: amax from the P partials, then codes of this workgroup's chunks;
 // workgroup 0 writes the scale and the codes of the tail.
-__global__ __launch_bounds__(kQuantThreads) void quantize_kernel(const uint16_t* __restrict__ x, long long n,
-                                                                 const float* __restrict__ partial, int P,
-                                                                 uint8_t* __restrict__ codes,
-                                                                 float* __restrict__ scale) {
+__global__ __launch_bounds__(kQuantThreads) void quantize_kernel(QuantBatch q) {
   __shared__ uint32_t sh[kQuantThreads / 64];
+  const uint16_t* __restrict__ x = q.x[blockIdx.y];
+  const float* __restrict__ partial = q.partial + (size_t)blockIdx.y * q.P;
+  uint8_t* __restrict__ codes = q.codes[blockIdx.y];
+  float* __restrict__ scale = q.scale + blockIdx.y;
+  const long long n = q.n;
+  const int P = q.P;
   uint32_t m = 0;
   for (int i = threadIdx.x; i < P; i += kQuantThreads) m = max(m, __builtin_bit_cast(uint32_t, partial[i]));
   m = block_max_u32(m, sh);
@@ -127,15 +134,23 @@ int quant_partial_blocks(long long n) {
   return (int)(b < 1 ? 1 : (b > kMaxPartials ? kMaxPartials : b));
 }
 
-hipError_t launch_quantize_fp8(const void* x, long long n, float* partial, uint8_t* codes, float* scale,
-                               hipStream_t stream) {
-  const int P = quant_partial_blocks(n);
+hipError_t launch_quantize_fp8(int count, const void* const* x, long long n, float* partial, void* const* codes,
+                               float* scales, hipStream_t stream) {
+  if (count < 1 || count > kQuantBatch) return hipErrorInvalidValue;
+  QuantBatch q = {};
+  for (int t = 0; t < count; ++t) {
+    q.x[t] = (const uint16_t*)x[t];
+    q.codes[t] = (uint8_t*)codes[t];
+  }
+  q.scale = scales;
+  q.partial = partial;
+  q.n = n;
+  q.P = quant_partial_blocks(n);
   const long long chunks = n / 8;
   long long g = (chunks + kQuantThreads - 1) / kQuantThreads;
   g = g < 1 ? 1 : (g > kMaxEncodeGroups ? kMaxEncodeGroups : g);
-  hipLaunchKernelGGL(amax_partial_kernel, dim3(P), dim3(kQuantThreads), 0, stream, (const uint16_t*)x, n, partial);
-  hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)g), dim3(kQuantThreads), 0, stream, (const uint16_t*)x, n,
-                     partial, P, codes, scale);
+  hipLaunchKernelGGL(amax_partial_kernel, dim3(q.P, count), dim3(kQuantThreads), 0, stream, q);
+  hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)g, count), dim3(kQuantThreads), 0, stream, q);
   return hipGetLastError();
 }
 
