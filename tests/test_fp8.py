@@ -165,6 +165,35 @@ def test_fp8qk_matches_oracle_on_dequantised_inputs(dev, causal, N):
     assert np.all(err <= tol)
 
 
+def _gpu_fp8_nonorm(codes, scales, v, lam_value, dev, causal):
+    g = {k: torch.from_numpy(codes[k]).to(dev) for k in codes}
+    lam_t = torch.tensor([lam_value], dtype=torch.float32, device=dev)
+    out = da.fwd_fp8qk(g["q1"], g["k1"], g["q2"], g["k2"], torch.from_numpy(scales).to(dev), v.to(dev), lam_t, 0.8,
+                       causal=causal, norm=False)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy()
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_fp8qk_without_norm(dev, causal):
+    # Eq. 1's Y = (A1 - lambda A2) V (the testing hook without the norm), to
+    # the bf16 path's 2e-2 on the dequantised inputs
+    x = W.prefill_inputs(1, 2, 190, D, "bf16", seed=81)
+    codes, scales, deq = _oracle_quant(x)
+    got = _gpu_fp8_nonorm(codes, scales, x["v"], 0.6, dev, causal)
+    ref = O.forward(deq["q1"], deq["k1"], deq["q2"], deq["k2"], x["v"], 0.6, 0.8, causal=causal, norm=False)
+    assert np.max(np.abs(got - ref)) <= 2e-2
+
+
+@pytest.mark.parametrize("lam_value", [-0.3, 0.5, 1.7])
+def test_fp8qk_rows_sum_to_one_minus_lambda(dev, lam_value):
+    # V = ones and no norm: every row of Y is 1 - lambda (each map's rows sum to 1)
+    x = W.prefill_inputs(1, 2, 130, D, "bf16", seed=82)
+    codes, scales, _ = _oracle_quant(x)
+    out = _gpu_fp8_nonorm(codes, scales, torch.ones_like(x["v"]), lam_value, dev, True)
+    assert np.max(np.abs(out - (1.0 - lam_value))) <= 4e-3
+
+
 @pytest.mark.parametrize("lam_value", [-0.3, 0.0, 1.0])
 def test_fp8qk_lambda_values(dev, lam_value):
     x = W.prefill_inputs(1, 3, 150, D, "bf16", seed=51)
