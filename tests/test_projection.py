@@ -54,7 +54,9 @@ def test_in_proj(dev, B, N, dm, H, d):
         _check(g, r, m, dm)
 
 
-OUT_CASES = [(2, 2, 77, 64, 256), (1, 3, 130, 32, 100), (2, 1, 33, 128, 4), (1, 4, 129, 16, 36)]
+# reduction lengths H*2d of 32 and 96 leave the last 64-wide step half empty
+OUT_CASES = [(2, 2, 77, 64, 256), (1, 3, 130, 32, 100), (2, 1, 33, 128, 4), (1, 4, 129, 16, 36),
+             (1, 1, 50, 16, 8), (2, 3, 20, 16, 12)]
 
 
 @pytest.mark.parametrize("B,H,N,d,dout", OUT_CASES)
