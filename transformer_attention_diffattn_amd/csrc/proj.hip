@@ -62,8 +62,8 @@ __global__ __launch_bounds__(256, 2) void proj_kernel(ProjArgs a) {
   // The workgroup's operand tiles pass through LDS, 64 reduction elements
   // (128 bytes per row) at a time, double-buffered: 128 feature rows of W
   // and 128 token rows of X, each row's eight 16-byte chunks XOR-swizzled by
-  // (row mod 8) so that the 16 rows one fragment read touches spread over
-  // all banks.  Thread t loads chunks t + 256u (u < 4) of each tile: eight
+  // (row mod 8) so that each eight consecutive rows of a fragment read fall
+  // on distinct 16-byte bank groups.  Thread t loads chunks t + 256u (u < 4) of each tile: eight
   // consecutive threads cover one row's 128 bytes.
   __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][kProjTile * 64];  // [buffer][W, X][row*64 + k]
   const int tid = threadIdx.x;
