@@ -334,7 +334,8 @@ def fp8_leg(args, stream, torch, da, W):
                      "end_to_end_ms": round(ms["quant"] + ms["fp8"], 4),
                      "roofline": {"bound": "hbm", "kernel": "amax_partial_kernel + quantize_kernel (4 tensors)",
                                   "achieved": round(qgbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                  "frac": round(qgbs / PEAK_HBM_GBS, 4), "traffic": None,
+                                  "frac": round(qgbs / PEAK_HBM_GBS, 4),
+                                  "traffic": _traffic("quant_fp8_layer3b", "quant.hip"),
                                   "algorithmic_bytes": qbytes}},
     }
 
