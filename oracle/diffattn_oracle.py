@@ -64,6 +64,7 @@ __all__ = [
     "map_stats",
     "backward",
     "backward_dq_rows",
+    "backward_dkv_keys",
 ]
 
 
@@ -327,3 +328,62 @@ def backward_dq_rows(q1, k1, q2, k2, v, rows, lq1, lk1, lq2, lk2, lambda_init: f
         dq1[r_i] = ds1 @ k1[:kmax] / math.sqrt(d)
         dq2[r_i] = ds2 @ k2[:kmax] / math.sqrt(d)
     return dq1, dq2
+
+
+def backward_dkv_keys(q1, k1, q2, k2, v, keys, lq1, lk1, lq2, lk2, lambda_init: float, dout,
+                      weight=None, eps: float = 1e-5, causal: bool = True, rows=None, block: int = 256):
+    """dK1, dK2 and dV of the given keys only, for one head, summed over the
+    query rows in ``rows`` (default: every row).
+
+    q1, k1, q2, k2: [N, d]; v, dout: [N, 2d]; keys: 1-D ints; rows: a range of
+    query rows (start, stop) or None.  The same chain rule as ``backward``,
+    read column-wise: key j's gradients are sums over the query rows i that
+    see it,
+
+      dV[j]   = sum_i (A1[i,j] - lambda A2[i,j]) dY_i
+      dK_k[j] = sum_i dS_k[i,j] Q_k[i] / sqrt d,
+      dS_1[i,j] = A1[i,j] (dY_i . V_j - dY_i . O1_i),
+      dS_2[i,j] = A2[i,j] (-lambda dY_i . V_j + lambda dY_i . O2_i),
+
+    where each row's A_k, O_k = A_k V and dY come from that row's own forward
+    against all the keys it sees.  A sum over rows splits exactly into sums
+    over row ranges, so a long sequence can be covered range by range (in
+    separate processes) and the partial results added.
+    Returns (dk1 [len(keys), d], dk2 [len(keys), d], dv [len(keys), 2d]).
+    """
+    q1, k1, q2, k2, v, g_out = (_f64(t) for t in (q1, k1, q2, k2, v, dout))
+    lam = lambda_scalar(lq1, lk1, lq2, lk2, lambda_init)
+    sigma = 1.0 - float(lambda_init)
+    N, d = q1.shape
+    n = v.shape[-1]
+    w = np.ones(n) if weight is None else _f64(weight)
+    keys = np.asarray(keys)
+    r_start, r_stop = (0, N) if rows is None else (int(rows[0]), int(rows[1]))
+    if causal:  # rows before the first sampled key see none of them
+        r_start = max(r_start, int(keys.min()))
+    dk1 = np.zeros((len(keys), d))
+    dk2 = np.zeros((len(keys), d))
+    dv = np.zeros((len(keys), n))
+    for r0 in range(r_start, r_stop, block):
+        rr = np.arange(r0, min(r_stop, r0 + block))
+        kmax = int(rr[-1]) + 1 if causal else N
+        vis = _visible(len(rr), kmax, causal, q_pos=rr)
+        a1 = softmax_rows(np.where(vis, (q1[rr] @ k1[:kmax].T) / math.sqrt(d), -np.inf))
+        a2 = softmax_rows(np.where(vis, (q2[rr] @ k2[:kmax].T) / math.sqrt(d), -np.inf))
+        o1 = a1 @ v[:kmax]
+        o2 = a2 @ v[:kmax]
+        y = o1 - lam * o2
+        r = np.sqrt(np.mean(y * y, axis=-1, keepdims=True) + float(eps))
+        g = sigma * w * g_out[rr]
+        dy = g / r - y * np.sum(g * y, axis=-1, keepdims=True) / (n * r ** 3)
+        sk = keys[keys < kmax]  # sampled keys inside this block's key range
+        idx = np.nonzero(keys < kmax)[0]
+        if len(sk) == 0:
+            continue
+        da = dy @ v[sk].T  # dL/dA1 at the sampled keys; dL/dA2 = -lambda da
+        ds1 = a1[:, sk] * (da - np.sum(dy * o1, axis=-1, keepdims=True))
+        ds2 = a2[:, sk] * (-lam * da + lam * np.sum(dy * o2, axis=-1, keepdims=True))
+        dk1[idx] += ds1.T @ q1[rr] / math.sqrt(d)
+        dk2[idx] += ds2.T @ q2[rr] / math.sqrt(d)
+        dv[idx] += (a1[:, sk] - lam * a2[:, sk]).T @ dy
+    return dk1, dk2, dv

@@ -5,14 +5,22 @@ TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only ``tests/``,
 import or call this module.  It shares no code with the HIP path and imports
 nothing from the package.
 
-The pages study attention whose logits come from low-bit queries and keys
-(page 3 = "Differential Transformer" sample peer review, reviewpaper.ai,
-"Strengths" and the low-bit attention-logit figure it discusses, Fig. 8: the
-differential map keeps its accuracy when Q and K are quantised with absmax
-scaling, where the plain softmax map degrades).  Here the low-bit format is
-the 8-bit e4m3 format of the OCP "8-bit floating point" specification (sign,
-4 exponent bits with bias 7, 3 mantissa bits; subnormals at exponent field 0;
-no infinities; 0x7F / 0xFF are NaN; largest finite value 448).
+What the pages say: the review page ("Differential Transformer" sample
+peer review, reviewpaper.ai) notes in "Strengths" that the differential map
+has far smaller attention-logit outliers (top-1 logits 38.8 against 318.0,
+Table 5) and cites a 4-bit quantisation study of the attention LOGITS
+(Fig. 8) as pointing to low-bit attention kernels; its "Questions" ask
+whether that study's absmax quantisation is applied to each of the two logit
+matrices separately, per head or per tensor.  The pages therefore quantise
+logits, not queries and keys, and give no format.
+
+This build's reading (an engineering one, not the pages'): the low-bit
+attention kernel that gfx950's matrix cores make worthwhile quantises the
+OPERANDS of the logit product, Q and K, to the 8-bit e4m3 format of the OCP
+"8-bit floating point" specification (sign, 4 exponent bits with bias 7, 3
+mantissa bits; subnormals at exponent field 0; no infinities; 0x7F / 0xFF
+are NaN; largest finite value 448), so that the logits are formed by the fp8
+product; the logits themselves stay fp32.
 
 Readings taken where the pages are silent (listed in the design notes):
 

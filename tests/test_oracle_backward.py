@@ -136,3 +136,47 @@ def test_backward_dk_sums_to_zero_over_keys():
                    x["lambda_init"], x["dout"], weight=x["weight"], eps=1e-5, causal=True)
     for k in ("dk1", "dk2"):
         assert np.max(np.abs(g[k].sum(axis=2))) < 1e-12 * max(1.0, np.max(np.abs(g[k])))
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_backward_dkv_keys_match_backward(causal):
+    """The key-wise dK1, dK2, dV (each key's sum over the query rows that
+    see it) equal the full backward's rows for those keys, at block sizes
+    that split the rows unevenly, and summed over a split into row ranges."""
+    x = _case(31, 1, 1, 53, 8)
+    g = O.backward(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], x["lq1"], x["lk1"], x["lq2"], x["lk2"],
+                   x["lambda_init"], x["dout"], weight=x["weight"], eps=1e-5, causal=causal)
+    keys = np.array([0, 1, 7, 26, 51, 52])
+    sl = lambda k: x[k][0, 0]
+    args = (sl("q1"), sl("k1"), sl("q2"), sl("k2"), sl("v"), keys, x["lq1"], x["lk1"], x["lq2"], x["lk2"],
+            x["lambda_init"], sl("dout"))
+    for block in (5, 16, 64):
+        dk1, dk2, dv = O.backward_dkv_keys(*args, weight=x["weight"], eps=1e-5, causal=causal, block=block)
+        for got, name in ((dk1, "dk1"), (dk2, "dk2"), (dv, "dv")):
+            ref = g[name][0, 0][keys]
+            assert np.max(np.abs(got - ref)) < 1e-12 * max(1.0, np.max(np.abs(ref))), (name, block)
+    parts = [O.backward_dkv_keys(*args, weight=x["weight"], eps=1e-5, causal=causal, rows=r, block=7)
+             for r in ((0, 20), (20, 33), (33, 53))]
+    for i, name in enumerate(("dk1", "dk2", "dv")):
+        got = sum(p[i] for p in parts)
+        ref = g[name][0, 0][keys]
+        assert np.max(np.abs(got - ref)) < 1e-12 * max(1.0, np.max(np.abs(ref))), name
+
+
+def test_backward_dkv_keys_last_key_sees_one_row():
+    """Causal: the last key is seen by the last query row only, so its dV is
+    D[N-1, N-1] dY_{N-1} -- checked against that row's own forward and dY
+    written out from Eq. 3's Jacobian."""
+    x = _case(37, 1, 1, 12, 4)
+    sl = lambda k: x[k][0, 0]
+    lam = O.lambda_scalar(x["lq1"], x["lk1"], x["lq2"], x["lk2"], x["lambda_init"])
+    _, _, dv = O.backward_dkv_keys(sl("q1"), sl("k1"), sl("q2"), sl("k2"), sl("v"), [11], x["lq1"], x["lk1"],
+                                   x["lq2"], x["lk2"], x["lambda_init"], sl("dout"), weight=x["weight"],
+                                   eps=1e-5, causal=True)
+    dmap = O.diff_weights(sl("q1"), sl("k1"), sl("q2"), sl("k2"), lam, causal=True)
+    y = dmap[11] @ sl("v")
+    n = y.size
+    r = math.sqrt(float(np.mean(y * y)) + 1e-5)
+    g = (1 - x["lambda_init"]) * x["weight"] * sl("dout")[11]
+    dy = g / r - y * float(np.dot(g, y)) / (n * r ** 3)
+    assert np.max(np.abs(dv[0] - dmap[11, 11] * dy)) < 1e-12
