@@ -92,7 +92,14 @@ DIFFATTN_API diffattn_status diffattn_lambda(const float* lq1, const float* lk1,
  *   eps            : added to mean(Y^2) inside the square root (>= 0)
  *   flags          : DIFFATTN_CAUSAL | DIFFATTN_NO_NORM
  * Softmax and all accumulation are fp32; for dt = BF16 the probabilities
- * enter the PV product rounded to bf16.
+ * enter the PV product rounded to bf16, except in rows that see no more
+ * than one key tile of keys (32 at d = 128, 64 below: the first rows of a
+ * causal head, every row of a sequence that short), where they enter as the
+ * sum of two bf16 terms (relative 2^-17) because the norm can amplify their
+ * rounding when the two maps nearly cancel.
+ * Size limit (dt = BF16): a head's output rows are addressed with 32-bit byte
+ * offsets, so N * 2d * 2 must stay below 2^31 (N < 4,194,304 at d = 128);
+ * larger N returns DIFFATTN_EINVAL.  B * H must fit an int.
  */
 DIFFATTN_API diffattn_status diffattn_fwd(diffattn_dtype dt, const void* q1, const void* k1, const void* q2,
                              const void* k2, const void* v, void* out, int B, int H, int N, int d,
@@ -199,10 +206,13 @@ DIFFATTN_API diffattn_status diffattn_lambda_bwd(const float* lq1, const float* 
                                     float* dlk1, float* dlq2, float* dlk2, void* stream);
 
 /*
- * fp8 (e4m3) query/key path: low-bit attention logits ("Differential
- * Transformer" sample peer review, "Strengths", and the low-bit
- * attention-logit figure it discusses, Fig. 8).  The format is OCP e4m3
- * (bias 7, no infinities, largest finite value 448).
+ * fp8 (e4m3) query/key path.  The "Differential Transformer" sample peer
+ * review ("Strengths", Table 5 and Fig. 8) reports smaller attention-logit
+ * outliers and a 4-bit quantisation study of the attention logits, pointing
+ * to low-bit attention kernels; it gives no format.  This path is an
+ * engineering reading of that: the logit product's operands Q and K are
+ * quantised (not the logits), to OCP e4m3 (bias 7, no infinities, largest
+ * finite value 448), so that the fp8 matrix cores form the logits in fp32.
  *
  * diffattn_quantize_fp8_workspace_bytes -- device scratch bytes that
  * diffattn_quantize_fp8 needs for n values (at most 1024; 0 for n < 0).

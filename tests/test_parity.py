@@ -298,21 +298,22 @@ def test_full_size_decode_sampled(dev):
     torch.cuda.empty_cache()
 
 
-def _rounding_bound(x, lam, causal):
-    """Per-element bound on |gpu - oracle| after the norm for bf16 inputs.
+def _rounding_sigma(x, lam, causal):
+    """Diagnostic only: six standard deviations of the output error that
+    rounding every softmax weight to bf16 would cause.
 
-    The kernel rounds each weight of both maps to bf16, an independent
-    relative error of standard deviation 2^-9/sqrt(3) each, so channel c of
-    a row's Y carries an error of standard deviation
+    A weight rounded to bf16 carries an independent relative error of
+    standard deviation 2^-9/sqrt(3), so channel c of a row's Y would carry
     sigma_c = 2^-9/sqrt(3) sqrt(sum_j (A1_ij^2 + lambda^2 A2_ij^2) V_jc^2),
     which the norm out = s w Y / r divides by r.  Where the two maps nearly
-    cancel (lambda near 1, few keys) r is small against the terms and six
-    such standard deviations (plus the output's own rounding) exceed the 2e-2
-    that holds elsewhere; the tolerance is the larger of the two."""
+    cancel (lambda near 1, few keys) r is small against the terms and this
+    exceeds 2e-2; the kernel carries the weights of such rows (those that
+    see no more than one key tile) as two bf16 terms, so the plain 2e-2
+    holds there too.  Printed next to the measured error."""
     s = 1.0 - x["lambda_init"]
     u = 2.0 ** -9
     B, H, N, d = x["q1"].shape
-    tol = np.empty((B, H, N, 2 * d))
+    sig = np.empty((B, H, N, 2 * d))
     for b in range(B):
         for h in range(H):
             sl = lambda t: O._f64(t[b, h])
@@ -321,9 +322,8 @@ def _rounding_bound(x, lam, causal):
             v = sl(x["v"])
             y = (a1 - lam * a2) @ v
             r = np.sqrt(np.mean(y * y, axis=1, keepdims=True) + x["eps"])
-            sig = u / np.sqrt(3.0) * np.sqrt((a1 * a1 + lam * lam * a2 * a2) @ (v * v))
-            tol[b, h] = np.maximum(TOL["bf16"], (6.0 * s * sig + u * s * np.abs(y)) / r)
-    return tol
+            sig[b, h] = 6.0 * s * u / np.sqrt(3.0) * np.sqrt((a1 * a1 + lam * lam * a2 * a2) @ (v * v)) / r
+    return sig
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -331,8 +331,9 @@ def _rounding_bound(x, lam, causal):
 @pytest.mark.parametrize("N", [15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129])
 def test_prefill_tile_boundaries(dev, d, causal, N):
     """Lengths on each side of the 16-row sub-tile, 32/64-key tile and
-    128-row item boundaries, several heads so items interleave; compared
-    row by row to the bf16 rounding bound (at least 2e-2)."""
+    128-row item boundaries, several heads so items interleave; every
+    element within the bf16 tolerance 2e-2 (the seeds include lambda near 1,
+    where the first rows' maps nearly cancel)."""
     print(f"case prefill boundary d={d} causal={causal} N={N}", flush=True)
     x = W.prefill_inputs(1, 3, N, d, "bf16", seed=3000 + N + d)
     lam = _lam_host(x)
@@ -340,7 +341,30 @@ def test_prefill_tile_boundaries(dev, d, causal, N):
     ref = O.forward(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam, x["lambda_init"], eps=x["eps"],
                     causal=causal)
     err = np.abs(out.float().cpu().numpy().astype(np.float64) - ref)
-    tol = _rounding_bound(x, lam, causal)
-    worst = np.unravel_index(np.argmax(err - tol), err.shape)
-    print(f"max err {err.max():.3e}; worst vs bound {err[worst]:.3e} / {tol[worst]:.3e} at {worst}", flush=True)
-    assert np.all(err <= tol), (err[worst], tol[worst], worst)
+    sig = _rounding_sigma(x, lam, causal)
+    worst = np.unravel_index(np.argmax(err), err.shape)
+    print(f"lambda {lam:.4f}: max err {err.max():.3e} at {worst}; six sigma of plain bf16 weights there "
+          f"{sig[worst]:.3e} (largest {sig.max():.3e})", flush=True)
+    assert err.max() <= TOL["bf16"], (err[worst], worst)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("lam_value", [0.97, 0.99, 1.0])
+def test_prefill_near_cancellation(dev, d, causal, lam_value):
+    """lambda set close to 1 on sequences no longer than one key tile (every
+    row sees at most 32 / 64 keys): A1 V and lambda A2 V nearly cancel and
+    the norm divides by a small rms(Y), so this is where the rounding of the
+    weights is amplified most (review page, "Weaknesses" and "Questions":
+    rows sum to 1 - lambda, the regime lambda ~ 1)."""
+    bn = 32 if d == 128 else 64
+    for N in (2, 5, bn):
+        x = W.prefill_inputs(1, 4, N, d, "bf16", seed=3500 + N + d)
+        out = _gpu_prefill(x, dev, causal=causal, lam_value=lam_value)
+        ref = O.forward(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam_value, x["lambda_init"], eps=x["eps"],
+                        causal=causal)
+        err = _maxerr(out.float().cpu().numpy(), ref)
+        sig = _rounding_sigma(x, lam_value, causal)
+        print(f"N={N} lambda={lam_value}: max err {err:.3e} (six sigma of plain bf16 weights up to "
+              f"{sig.max():.3e})", flush=True)
+        assert err <= TOL["bf16"], (N, err)

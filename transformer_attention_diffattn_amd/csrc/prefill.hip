@@ -110,11 +110,9 @@ struct Bf16Cfg {
   static constexpr int SUB = 2;
   static constexpr int BN = D >= 128 ? 32 : 64;  // d = 128: keeps a wave within 256 registers
   // Software-pipelined tile loop (QK^T of the next tile overlaps the
-  // softmax of the current one); the sequential tile body stays as the
-  // alternative for shapes whose second score tile would not fit in
-  // registers.
-  static constexpr bool PIPE = D <= 128;
-  static constexpr int STAGES = PIPE ? 3 : 2;  // LDS stage buffers
+  // softmax of the current one): tiles t and t+1 are read while t+2 loads,
+  // so three LDS stage buffers.
+  static constexpr int STAGES = 3;
   static constexpr int PV_FENCE = D >= 128 ? 4 : 0;  // channel blocks between scheduling fences
   // LDS fragment reads issued ahead of their MFMAs in the pipelined loop
   static constexpr int K_AHEAD = 1;  // 16-key blocks of K
@@ -133,10 +131,9 @@ struct Bf16Tile {
   static constexpr int BM = 16 * SUB * (WAVES / 2);
   static constexpr int BN = Bf16Cfg<D>::BN;
   static constexpr int STAGES = Bf16Cfg<D>::STAGES;
-  static constexpr bool PIPE = Bf16Cfg<D>::PIPE;
   static constexpr int K_AHEAD = Bf16Cfg<D>::K_AHEAD;
   static constexpr int V_AHEAD = Bf16Cfg<D>::V_AHEAD;
-  static_assert(STAGES >= (PIPE ? 3 : 2), "stage ring of the tile loop");
+  static_assert(STAGES >= 3, "stage ring of the pipelined tile loop");
   static constexpr int PV_FENCE = Bf16Cfg<D>::PV_FENCE;
   static constexpr int KS = F8 ? 1 : (D + 31) / 32;  // k-steps of the QK^T MFMA
   static constexpr int NB = BN / 16;        // 16-key score blocks per tile
@@ -427,8 +424,9 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
     rescale(mt, need);
   };
 
-  // O^T += V^T P^T
-  auto pv = [&](const uint16_t* stg, const PFrags& pf) {
+  // O^T += V^T P^T.  With a second set of fragments (lo), each V fragment
+  // read also feeds O^T += V^T lo^T: P enters as the sum of two bf16 terms.
+  auto pv = [&](const uint16_t* stg, const PFrags& pf, const PFrags& lo, bool split) {
     const uint16_t* vs = stg + 2 * KTILE;
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) {
@@ -447,13 +445,17 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
         const bf16x8 va = as_bf16x8(vu);
 #pragma unroll
         for (int u = 0; u < SUB; ++u) O[u][cb] = mfma16x16x32_bf16(va, pf[cc][u], O[u][cb]);
+        if (split) {
+#pragma unroll
+          for (int u = 0; u < SUB; ++u) O[u][cb] = mfma16x16x32_bf16(va, lo[cc][u], O[u][cb]);
+        }
         // keep the scheduler from hoisting every V fragment read at once
         if (T::PV_FENCE > 0 && cb % T::PV_FENCE == T::PV_FENCE - 1) __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
 
-  // ---- pieces of the software-pipelined iteration (d <= 64) ----
+  // ---- pieces of the software-pipelined iteration ----
   // There a tile's scores are kept as t = s c - m (log2 units, -inf where
   // masked): the row maxima are then taken over FMA results, which need no
   // canonicalisation, and a rescale only shifts t.  Each group of
@@ -499,6 +501,25 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
       const float* tp = &t[u][4 * (2 * cc + h)];
       pu[2 * h] = pack_bf16x2(exp2_fast(tp[0]), exp2_fast(tp[1]));
       pu[2 * h + 1] = pack_bf16x2(exp2_fast(tp[2]), exp2_fast(tp[3]));
+    }
+    return as_bf16x8(pu);
+  };
+
+  // The bf16 remainder P - bf16(P) of chunk q of the exponentiated tile e.
+  // P - bf16(P) is exact in fp32 (at most 16 significant bits), so
+  // bf16(P) + bf16(P - bf16(P)) carries P to a relative 2^-17 instead of the
+  // 2^-9 of bf16(P) alone.
+  auto pack_lo_chunk = [&](const Scores& e, int q) {
+    const int cc = q / SUB, u = q % SUB;
+    u32x4 pu;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float* ep = &e[u][4 * (2 * cc + h)];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const uint32_t hi = pack_bf16x2(ep[2 * k], ep[2 * k + 1]);
+        pu[2 * h + k] = pack_bf16x2(ep[2 * k] - bf16_lo(hi), ep[2 * k + 1] - bf16_hi(hi));
+      }
     }
     return as_bf16x8(pu);
   };
@@ -621,64 +642,6 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
   auto visible_tiles = [&](const Item& it) {
     if (it.qw0 >= N) return 0;
     return CAUSAL ? min(it.nkt, (it.qw0 + 16 * SUB - 1) / BN + 1) : it.nkt;
-  };
-
-  // t = s c - m of a whole raw tile (-inf where masked) and its row maxima;
-  // returns whether some row needs a new reference
-  auto scale_max = [&](Scores& sc, int kb, int qw0, float (&mt)[SUB], auto mask_tag) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    bool need = false;
-#pragma unroll
-    for (int u = 0; u < SUB; ++u) {
-      const int last_key = CAUSAL ? min(qw0 + 16 * u + lr, N - 1) : N - 1;
-      const int lim = last_key - kb - 4 * lg;
-      float mx = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 4 * NB; ++i) {
-        float x = __builtin_fmaf(sc[u][i], c, -m[u]);
-        if (MASK) x = (16 * (i / 4) + (i % 4) <= lim) ? x : -INFINITY;
-        sc[u][i] = x;
-        mx = fmaxf(mx, x);
-      }
-      mt[u] = max4_groups(mx);
-      need |= mt[u] > kRescaleThreshold;
-    }
-    return need;
-  };
-
-  // One tile, phases in sequence.  The first tile of an item sets the
-  // references from its exact maxima; later ones work on t = s c - m.
-  auto compute_tile = [&](const uint16_t* stg, const Item& it, int kt) {
-    const int kb = kt * BN;
-    if (kt >= visible_tiles(it)) return;  // nothing visible for this wave
-    Scores sc;
-    PFrags pf;
-    if (kt == 0) {
-      if (tile_masked(it, kb))
-        qk(sc, stg, kb, it.qw0, std::true_type{});
-      else
-        qk(sc, stg, kb, it.qw0, std::false_type{});
-      update_max(sc);
-#pragma unroll
-      for (int u = 0; u < SUB; ++u)
-#pragma unroll
-        for (int i = 0; i < 4 * NB; ++i) sc[u][i] = __builtin_fmaf(sc[u][i], c, -m[u]);
-    } else {
-      qk(sc, stg, kb, it.qw0, std::false_type{});
-      float mt[SUB];
-      bool need;
-      if (tile_masked(it, kb))
-        need = scale_max(sc, kb, it.qw0, mt, std::true_type{});
-      else
-        need = scale_max(sc, kb, it.qw0, mt, std::false_type{});
-      rescale_t(sc, mt, need);
-    }
-#pragma unroll
-    for (int q = 0; q < NC * SUB; ++q) {
-      pf[q / SUB][q % SUB] = p_chunk(sc, q);
-      L[q % SUB] = mfma16x16x32_bf16(ones, pf[q / SUB][q % SUB], L[q % SUB]);
-    }
-    pv(stg, pf);
   };
 
   // Epilogue of one item.  The two waves of a row group (one per map) each
@@ -831,7 +794,7 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
   };
   // Tiles loading ahead of the one made available next: the pipelined loop
   // reads two tiles at a time, so one buffer fewer is free for loads.
-  constexpr int LOOK = T::PIPE ? STAGES - 2 : STAGES - 1;
+  constexpr int LOOK = STAGES - 2;
   int ib = 0;       // stage buffer of the next tile to load
   int pending = 0;  // tiles loading and not yet made available
   auto load_next = [&](Cursor& q) {
@@ -900,7 +863,7 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
       L[u] = zero_f32x4();
       m[u] = -INFINITY;
     }
-    if constexpr (T::PIPE) {
+    {
       // Iteration kt forms P of tile kt (VALU) while the QK^T products of
       // tile kt+1 run on the matrix cores, then runs PV of tile kt while the
       // row maxima of tile kt+1 are taken.  Tiles kt and kt+1 are read
@@ -923,18 +886,34 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
         const bool need = phase_b(bc + 2 * KTILE, sc, sn, (kt + 1) * BN, cur.qw0, mt, mask_tag);
         rescale_t(sn, mt, need);
       };
-      // last visible tile of this wave: P and PV only
-      auto last = [&](int kt, const Scores& t) {
+      // last visible tile of this wave: P and PV only.  When it is also the
+      // wave's only one (every row sees at most BN keys: the first rows of a
+      // causal head, or a sequence no longer than a tile), P enters the
+      // products as bf16(P) + bf16(P - bf16(P)).  Those rows have few keys,
+      // and where the two maps nearly cancel (lambda near 1) the norm divides
+      // by an rms(Y) far below the size of A1 V and lambda A2 V, which would
+      // amplify the bf16 rounding of P beyond the output tolerance.  Rows
+      // with more keys average that rounding out.
+      auto last = [&](int kt, Scores& t) {
         const uint16_t* bc = stages + tb * T::STAGE;
         tb = next_buf(tb);
         if (kt + 1 < cur.nkt) avail(ld);
-        PFrags pf;
+        const bool split = kt == 0;
+#pragma unroll
+        for (int u = 0; u < SUB; ++u)
+#pragma unroll
+          for (int i = 0; i < 4 * NB; ++i) t[u][i] = exp2_fast(t[u][i]);
+        PFrags pf, lo;
 #pragma unroll
         for (int q = 0; q < NC * SUB; ++q) {
-          pf[q / SUB][q % SUB] = p_chunk(t, q);
+          pf[q / SUB][q % SUB] = pack_chunk(t, q);
           L[q % SUB] = mfma16x16x32_bf16(ones, pf[q / SUB][q % SUB], L[q % SUB]);
+          if (split) {
+            lo[q / SUB][q % SUB] = pack_lo_chunk(t, q);
+            L[q % SUB] = mfma16x16x32_bf16(ones, lo[q / SUB][q % SUB], L[q % SUB]);
+          }
         }
-        pv(bc, pf);
+        pv(bc, pf, lo, split);
       };
       // this wave's visible tiles: the first nfree carry no mask, the rest
       // (the diagonal and the ragged end) do
@@ -971,12 +950,6 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
       for (; kt < cur.nkt; ++kt) {  // tiles no row of this wave sees
         tb = next_buf(tb);
         if (kt + 1 < cur.nkt) avail(ld);
-      }
-    } else {
-      for (int kt = 0; kt < cur.nkt; ++kt) {
-        avail(ld);
-        compute_tile(stages + tb * T::STAGE, cur, kt);
-        tb = next_buf(tb);
       }
     }
     const int ni = item_at(r + 1);
