@@ -83,6 +83,19 @@ def test_fwd_validation(L):
     assert _fwd(L, B=65535, H=65535, N=1 << 20) == b.EINVAL
 
 
+def test_fwd_refuses_heads_past_32bit_offsets(L):
+    """The bf16 kernel addresses a head's output rows with 32-bit byte
+    offsets: N * 2d * 2 bytes must stay below 2^31.  The first N past that
+    limit is refused before any launch, for every bf16 prefill entry point."""
+    for d in (16, 32, 64, 128):
+        n_bad = (1 << 31) // (4 * d)  # N * 2d * 2 == 2^31
+        assert _fwd(L, d=d, N=n_bad) == b.EINVAL, d
+        assert _fwd(L, d=d, N=(1 << 31) - 1) == b.EINVAL, d
+        if d >= 32:
+            assert _fwd_train(L, d=d, N=n_bad) == b.EINVAL, d
+    assert _fp8(L, N=(1 << 31) // 512) == b.EINVAL
+
+
 def test_fwd_empty_work_is_ok_without_launch(L):
     assert _fwd(L, B=0) == b.OK
     assert _fwd(L, H=0) == b.OK

@@ -85,6 +85,30 @@ def _dev(t: torch.Tensor, name: str) -> torch.Tensor:
     return t
 
 
+def _like(t, name: str, shape, dtype, device) -> torch.Tensor:
+    """A caller-supplied output: on the device, contiguous, exactly this
+    shape and dtype (the C ABI cannot see buffer sizes)."""
+    _dev(t, name)
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != device:
+        raise ValueError(f"{name} must be a {dtype} tensor of shape {tuple(shape)} on {device}")
+    return t
+
+
+def _workspace(ws, name: str, device) -> int:
+    """A caller-supplied workspace on the device: returns its size in bytes."""
+    _dev(ws, name)
+    if ws.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    return ws.numel() * ws.element_size()
+
+
+def _weight(weight, d):
+    if weight is not None:
+        _dev(weight, "weight")
+        if weight.dtype != torch.float32 or weight.shape != (2 * d,):
+            raise ValueError("weight must be fp32 [2d]")
+
+
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -122,16 +146,11 @@ def fwd(q1, k1, q2, k2, v, lam_t, lambda_init: float, weight=None, eps: float = 
         raise ValueError("v must be [B,H,N,2d] of q1's dtype")
     if lam_t.dtype != torch.float32:
         raise ValueError("lambda must be fp32")
-    if weight is not None:
-        _dev(weight, "weight")
-        if weight.dtype != torch.float32 or weight.shape != (2 * d,):
-            raise ValueError("weight must be fp32 [2d]")
+    _weight(weight, d)
     if out is None:
         out = torch.empty_like(v)
     else:
-        _dev(out, "out")
-        if out.shape != v.shape or out.dtype != v.dtype:
-            raise ValueError("out must match v")
+        _like(out, "out", v.shape, v.dtype, v.device)
     flags = (CAUSAL if causal else 0) | (0 if norm else NO_NORM)
     _check(lib().diffattn_fwd(_DT[q1.dtype], _ptr(q1), _ptr(k1), _ptr(q2), _ptr(k2), _ptr(v), _ptr(out),
                               B, H, N, d, _ptr(lam_t), float(lambda_init), _ptr(weight), float(eps), flags,
@@ -171,11 +190,13 @@ def decode(q1, q2, k1c, k2c, vc, lam_t, lambda_init: float, cache_len=None, weig
     need = decode_workspace_bytes(B, H, L, d)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q1.device)
+    ws_bytes = _workspace(workspace, "workspace", q1.device)
     if out is None:
         out = torch.empty((B, H, 1, 2 * d), dtype=q1.dtype, device=q1.device)
+    _like(out, "out", (B, H, 1, 2 * d), q1.dtype, q1.device)
     _check(lib().diffattn_decode(_DT[q1.dtype], _ptr(q1), _ptr(q2), _ptr(k1c), _ptr(k2c), _ptr(vc),
                                  _ptr(cache_len), _ptr(out), B, H, L, d, _ptr(lam_t), float(lambda_init),
-                                 _ptr(weight), float(eps), _ptr(workspace), workspace.numel(),
+                                 _ptr(weight), float(eps), _ptr(workspace), ws_bytes,
                                  _stream(q1.device)), "diffattn_decode")
     return out
 
@@ -200,8 +221,9 @@ def fwd_train(q1, k1, q2, k2, v, lam_t, lambda_init: float, weight=None, eps: fl
     log2 units, o12 [2,B,H,N,2d] fp32 per-map outputs)."""
     B, H, N, d = _check_qkv(q1, k1, q2, k2, v)
     _dev(lam_t, "lambda")
-    if weight is not None:
-        _dev(weight, "weight")
+    if lam_t.dtype != torch.float32:
+        raise ValueError("lambda must be fp32")
+    _weight(weight, d)
     out = torch.empty_like(v)
     lse = torch.empty((2, B, H, N), dtype=torch.float32, device=q1.device)
     o12 = torch.empty((2, B, H, N, 2 * d), dtype=torch.float32, device=q1.device)
@@ -227,22 +249,30 @@ def bwd(q1, k1, q2, k2, v, dout, lse, o12, lam_t, lambda_init: float, weight=Non
         raise ValueError("dout must match v")
     if lse.shape != (2, B, H, N) or o12.shape != (2, B, H, N, 2 * d):
         raise ValueError("lse / o12 must come from fwd_train on the same shapes")
-    if weight is not None:
-        _dev(weight, "weight")
+    if lse.dtype != torch.float32 or o12.dtype != torch.float32 or lam_t.dtype != torch.float32:
+        raise ValueError("lse, o12 and lambda must be fp32")
+    _weight(weight, d)
     dev = q1.device
     if grads is None:
         grads = dict(dq1=torch.empty_like(q1), dk1=torch.empty_like(k1), dq2=torch.empty_like(q2),
                      dk2=torch.empty_like(k2), dv=torch.empty_like(v),
                      dlambda=torch.empty(1, dtype=torch.float32, device=dev),
                      dweight=torch.empty(2 * d, dtype=torch.float32, device=dev))
+    for k, shape, dt in (("dq1", q1.shape, q1.dtype), ("dk1", q1.shape, q1.dtype), ("dq2", q1.shape, q1.dtype),
+                         ("dk2", q1.shape, q1.dtype), ("dv", v.shape, v.dtype), ("dlambda", (1,), torch.float32),
+                         ("dweight", (2 * d,), torch.float32)):
+        if k not in grads:
+            raise ValueError(f"grads must hold {k}")
+        _like(grads[k], k, shape, dt, dev)
     if workspace is None:
         workspace = torch.empty(max(bwd_workspace_bytes(B, H, N, d), 256), dtype=torch.uint8, device=dev)
+    ws_bytes = _workspace(workspace, "workspace", dev)
     g = grads
     _check(lib().diffattn_bwd(BF16, _ptr(q1), _ptr(k1), _ptr(q2), _ptr(k2), _ptr(v), _ptr(dout), _ptr(lse),
                               _ptr(o12), B, H, N, d, _ptr(lam_t), float(lambda_init), _ptr(weight), float(eps),
                               CAUSAL if causal else 0, _ptr(g["dq1"]), _ptr(g["dk1"]), _ptr(g["dq2"]),
                               _ptr(g["dk2"]), _ptr(g["dv"]), _ptr(g["dlambda"]), _ptr(g["dweight"]),
-                              _ptr(workspace), workspace.numel(), _stream(dev)), "diffattn_bwd")
+                              _ptr(workspace), ws_bytes, _stream(dev)), "diffattn_bwd")
     return grads
 
 
@@ -250,6 +280,13 @@ def lambda_bwd(lq1, lk1, lq2, lk2, dlambda):
     """Eq. 2 backward: (dlq1, dlk1, dlq2, dlk2), fp32 [d] each."""
     for n, t in (("lq1", lq1), ("lk1", lk1), ("lq2", lq2), ("lk2", lk2), ("dlambda", dlambda)):
         _dev(t, n)
+        if t.dtype != torch.float32:
+            raise ValueError(f"{n} must be fp32")
+    for n, t in (("lk1", lk1), ("lq2", lq2), ("lk2", lk2)):
+        if t.shape != lq1.shape or lq1.dim() != 1:
+            raise ValueError(f"{n} must be fp32 [d] like lq1")
+    if dlambda.numel() != 1:
+        raise ValueError("dlambda must be fp32 [1]")
     outs = [torch.empty_like(lq1) for _ in range(4)]
     _check(lib().diffattn_lambda_bwd(_ptr(lq1), _ptr(lk1), _ptr(lq2), _ptr(lk2), lq1.numel(), _ptr(dlambda),
                                      *[_ptr(o) for o in outs], _stream(lq1.device)), "diffattn_lambda_bwd")
@@ -272,17 +309,18 @@ def quantize_fp8(x, codes=None, scale=None, workspace=None):
         codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     else:
         _dev(codes, "codes")
-        if codes.dtype != torch.uint8 or codes.numel() != n:
-            raise ValueError("codes must be uint8 with x's element count")
+        if codes.dtype != torch.uint8 or codes.numel() != n or codes.device != x.device:
+            raise ValueError("codes must be uint8 with x's element count on x's device")
     if scale is None:
         scale = torch.empty(1, dtype=torch.float32, device=x.device)
-    elif scale.dtype != torch.float32 or scale.numel() != 1 or scale.device.type != "cuda":
-        raise ValueError("scale must be one fp32 element on a HIP device")
+    elif scale.dtype != torch.float32 or scale.numel() != 1 or scale.device != x.device:
+        raise ValueError("scale must be one fp32 element on x's device")
     need = quantize_fp8_workspace_bytes(n)
     if workspace is None:
         workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=x.device)
+    ws_bytes = _workspace(workspace, "workspace", x.device)
     _check(lib().diffattn_quantize_fp8(_ptr(x), n, _ptr(codes), _ptr(scale), _ptr(workspace),
-                                       workspace.numel() * workspace.element_size(), _stream(x.device)),
+                                       ws_bytes, _stream(x.device)),
            "diffattn_quantize_fp8")
     return codes, scale
 
@@ -301,22 +339,25 @@ def quantize_fp8_batch(xs, codes=None, scales=None, workspace=None):
     dev = xs[0].device
     if codes is None:
         codes = [torch.empty(x.shape, dtype=torch.uint8, device=dev) for x in xs]
+    if len(codes) != count:
+        raise ValueError("one codes tensor per input")
     for k, c in enumerate(codes):
         _dev(c, f"codes[{k}]")
-        if c.dtype != torch.uint8 or c.numel() != n:
-            raise ValueError("codes must be uint8 with x's element count")
+        if c.dtype != torch.uint8 or c.numel() != n or c.device != dev:
+            raise ValueError("codes must be uint8 with x's element count on x's device")
     if scales is None:
         scales = torch.empty(count, dtype=torch.float32, device=dev)
     _dev(scales, "scales")
-    if scales.dtype != torch.float32 or scales.numel() != count:
-        raise ValueError("scales must be fp32 [count]")
+    if scales.dtype != torch.float32 or scales.numel() != count or scales.device != dev:
+        raise ValueError("scales must be fp32 [count] on x's device")
     need = count * quantize_fp8_workspace_bytes(n)
     if workspace is None:
         workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=dev)
+    ws_bytes = _workspace(workspace, "workspace", dev)
     xp = (ctypes.c_void_p * count)(*(x.data_ptr() for x in xs))
     cp = (ctypes.c_void_p * count)(*(c.data_ptr() for c in codes))
     _check(lib().diffattn_quantize_fp8_batch(count, xp, n, cp, _ptr(scales), _ptr(workspace),
-                                             workspace.numel() * workspace.element_size(), _stream(dev)),
+                                             ws_bytes, _stream(dev)),
            "diffattn_quantize_fp8_batch")
     return codes, scales
 
@@ -338,16 +379,11 @@ def fwd_fp8qk(q1, k1, q2, k2, qk_scale, v, lam_t, lambda_init: float, weight=Non
         raise ValueError("v must be bf16 [B,H,N,2d]")
     if lam_t.dtype != torch.float32:
         raise ValueError("lambda must be fp32")
-    if weight is not None:
-        _dev(weight, "weight")
-        if weight.dtype != torch.float32 or weight.shape != (2 * d,):
-            raise ValueError("weight must be fp32 [2d]")
+    _weight(weight, d)
     if out is None:
         out = torch.empty_like(v)
     else:
-        _dev(out, "out")
-        if out.shape != v.shape or out.dtype != v.dtype:
-            raise ValueError("out must match v")
+        _like(out, "out", v.shape, v.dtype, v.device)
     flags = (CAUSAL if causal else 0) | (0 if norm else NO_NORM)
     _check(lib().diffattn_fwd_fp8qk(_ptr(q1), _ptr(k1), _ptr(q2), _ptr(k2), _ptr(qk_scale), _ptr(v), _ptr(out),
                                     B, H, N, d, _ptr(lam_t), float(lambda_init), _ptr(weight), float(eps),
@@ -368,8 +404,12 @@ def in_proj(x, w_qkv, H: int, d: int, outs=None):
     if outs is None:
         outs = tuple(torch.empty((B, H, N, d), dtype=torch.bfloat16, device=x.device) for _ in range(4)) + (
             torch.empty((B, H, N, 2 * d), dtype=torch.bfloat16, device=x.device),)
+    if len(outs) != 5:
+        raise ValueError("outs must be (q1, k1, q2, k2, v)")
     for n, t in zip(("q1", "k1", "q2", "k2", "v"), outs):
-        _dev(t, n)
+        _like(t, n, (B, H, N, 2 * d if n == "v" else d), torch.bfloat16, x.device)
+    if w_qkv.device != x.device:
+        raise ValueError("w_qkv must be on x's device")
     _check(lib().diffattn_in_proj(_ptr(x), _ptr(w_qkv), B, N, dm, H, d, *(_ptr(t) for t in outs),
                                   _stream(x.device)), "diffattn_in_proj")
     return outs
@@ -384,9 +424,11 @@ def out_proj(o, w_o, out=None):
     B, H, N, dv = o.shape
     if w_o.dim() != 2 or w_o.shape[1] != H * dv:
         raise ValueError("w_o must be [d_out, H*2d]")
+    if w_o.device != o.device:
+        raise ValueError("w_o must be on o's device")
     if out is None:
         out = torch.empty((B, N, w_o.shape[0]), dtype=torch.bfloat16, device=o.device)
-    _dev(out, "out")
+    _like(out, "out", (B, N, w_o.shape[0]), torch.bfloat16, o.device)
     _check(lib().diffattn_out_proj(_ptr(o), _ptr(w_o), B, H, N, dv // 2, w_o.shape[0], _ptr(out),
                                    _stream(o.device)), "diffattn_out_proj")
     return out

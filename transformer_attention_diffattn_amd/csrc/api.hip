@@ -97,6 +97,9 @@ static diffattn_status fwd_impl(diffattn_dtype dt, const void* q1, const void* k
   // one workgroup per (query tile, head); a launch holds at most 2^32 - 1 work-items
   if (BH > INT32_MAX || qtiles * BH * diffattn::prefill_block_threads(bf16, d) > (long long)UINT32_MAX)
     return DIFFATTN_EINVAL;
+  // the bf16 kernel stores a head's output rows through a buffer resource
+  // with 32-bit byte offsets: the head's N x 2d bf16 outputs must stay below 2^31 bytes
+  if (bf16 && (long long)N * 2 * d * 2 > (long long)INT32_MAX) return DIFFATTN_EINVAL;
 
   diffattn::PrefillArgs a;
   a.q1 = q1;
