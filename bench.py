@@ -2,16 +2,19 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
-One step = diffattn_lambda + diffattn_fwd over the 1.4B-scale layer workload
-(bf16, B=4, H=16, N=2048, d=64, V width 128, causal).  Prints ONE JSON line:
-the whole-step throughput in TFLOP/s (12 d flops per causal query/key pair),
-the prefill kernel's roofline fraction against the bf16 dense MFMA peak, the
-CPU fp64 oracle timed on a bounded sample of the same workload, and a decode
-leg (diffattn_decode on 64 sequences x 16 heads x 32768 cached keys, d=128)
-reported in HBM GB/s against the 8 TB/s peak, and a training leg
-(diffattn_fwd_train + diffattn_bwd on the prefill workload).  Inputs are seeded synthetic
-tensors already resident in HBM when timing starts.  The prefill step is
-replayed from a HIP graph (checked equal to the eager step) so that host
+One step = diffattn_lambda + diffattn_fwd over the 64K-token prefill (bf16,
+B=1, H=12, N=65536, d=128, V width 256, causal, with needles): the largest
+prefill workload that fits one GPU.  Prints ONE JSON line: the whole-step
+throughput in TFLOP/s (12 d flops per causal query/key pair), the prefill
+kernel's roofline fraction against the bf16 dense MFMA peak, the CPU fp64
+oracle timed on a bounded sample of the same workload (sampled rows,
+extrapolated per pair), and beside them: the 1.4B- and 3B-scale layer
+prefills (each with its own roofline), a decode leg (diffattn_decode on 64
+sequences x 16 heads x 32768 cached keys, d=128) in HBM GB/s against the
+8 TB/s peak, a training leg (diffattn_fwd_train + diffattn_bwd on the 1.4B
+layer), the fp8 query/key prefill and the projections.  Inputs are seeded
+synthetic tensors already resident in HBM when timing starts.  Prefill steps
+are replayed from HIP graphs (checked equal to the eager step) so that host
 launch overhead does not idle the GPU; kernel durations come from HIP events
 on the stream the kernels run on.
 """
@@ -19,7 +22,6 @@ on the stream the kernels run on.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -34,24 +36,18 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "diff-attn fwd TFLOP/s & % bf16 MFMA peak (prefill); decode HBM GB/s & % peak"
 
 
-def _src_hash(*names):
-    h = hashlib.sha256()
-    for n in names:
-        with open(os.path.join(ROOT, "transformer_attention_diffattn_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
-
-
 def _traffic(kind: str, src: str):
     """Per-launch HBM bytes from the committed counter summary, if it was
-    taken on the current kernel source; else None."""
+    taken on the current kernel source and headers; else None."""
+    from transformer_attention_diffattn_amd.traffic_summary import source_hash
+
     path = os.path.join(ROOT, "profiles", f"{kind}_traffic.json")
     try:
         with open(path) as f:
             t = json.load(f)
     except OSError:
         return None
-    return t.get("bytes_per_launch") if t.get("source_sha256_16") == _src_hash(src) else None
+    return t.get("bytes_per_launch") if t.get("source_sha256_16") == source_hash(src) else None
 
 
 def _graph(fn, torch):
@@ -96,6 +92,71 @@ def _timed(replay, n, stream, torch):
     return e0.elapsed_time(e1)
 
 
+def prefill_leg(w, x, steps, warmup, prewarm_s, stream, torch, da, W):
+    """One prefill workload: diffattn_lambda + diffattn_fwd per step, replayed
+    from a HIP graph of R consecutive steps (checked equal to the eager step),
+    timed with HIP events on the stream the kernels run on.  Returns the
+    leg's figures and the lambda launch's own time."""
+    lam_t = torch.empty(1, device=x["q1"].device, dtype=torch.float32)
+    out = torch.empty_like(x["v"])
+
+    def step():
+        da.lam(x["lq1"], x["lk1"], x["lq2"], x["lk2"], x["lambda_init"], out=lam_t)
+        da.fwd(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam_t, x["lambda_init"], eps=x["eps"],
+               causal=w.causal, out=out)
+
+    # One graph holds R consecutive steps (each exactly the eager step's two
+    # library launches) and is replayed steps / R times, so one host launch
+    # covers R steps and the host's per-call overhead does not idle the GPU.
+    R = next(r for r in (20, 10, 8, 5, 4, 2, 1) if steps % r == 0)
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+
+    def lams_r():
+        for _ in range(R):
+            da.lam(x["lq1"], x["lk1"], x["lq2"], x["lk2"], x["lambda_init"], out=lam_t)
+
+    g_step = _graph(lambda: [step() for _ in range(R)], torch)
+    g_lam = _graph(lams_r, torch)
+    _prewarm(g_step.replay, prewarm_s, torch)
+    for _ in range(-(-warmup // R)):
+        g_step.replay()
+    total_ms = _timed(g_step.replay, steps // R, stream, torch)
+    if not torch.equal(out, eager):
+        raise RuntimeError(f"graph replay of the {w.name} step differs from the eager step")
+    # The dominant kernel's own time in the same launch configuration: the
+    # step less its lambda launch, timed alone the same way.  (Forward
+    # launches replayed back to back with nothing between them run slower:
+    # each persistent grid then starts on compute units as the previous one
+    # releases them, unevenly.)
+    for _ in range(-(-warmup // R)):
+        g_lam.replay()
+    lam_ms = _timed(g_lam.replay, steps // R, stream, torch) / steps
+    ms_step = total_ms / steps
+    kern_ms = ms_step - lam_ms
+    flops = 12.0 * w.d * w.pairs() * w.B * w.H
+    value = flops / (ms_step * 1e-3) / 1e12
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    leg = {
+        "value": round(value, 2), "ms_per_step": round(ms_step, 4), "steps_per_graph": R,
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "v_width": 2 * w.d,
+                   "causal": w.causal, "lambda_init": x["lambda_init"],
+                   "flops_per_pair": 12 * w.d, "pairs_per_head": w.pairs(),
+                   "needle_offsets": list(w.needle_offsets)},
+        "roofline": {"bound": "mfma", "kernel": f"prefill_bf16_kernel<{w.d},{'causal' if w.causal else 'full'},norm>",
+                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": (_traffic(W.PREFILL_TRAFFIC[w.name], "prefill.hip")
+                                 if w.name in W.PREFILL_TRAFFIC else None),
+                     # Q1, K1, Q2, K2 (4d) and V (2d) read once, out (2d) written once: 16 d bytes a row
+                     "algorithmic_bytes": 16 * w.d * w.N * w.B * w.H,
+                     "kernel_ms": round(kern_ms, 4), "lambda_ms": round(lam_ms, 5)},
+    }
+    del out
+    return leg, lam_ms
+
+
 def cpu_baseline(x, w, budget_s: float):
     """The oracle as it stands, on whole heads of the same inputs, until
     ``budget_s`` seconds of host time are spent."""
@@ -109,15 +170,17 @@ def cpu_baseline(x, w, budget_s: float):
     done = 0
     t0 = time.perf_counter()
     if w.N > 8192:
-        # long sequences: evenly spaced query rows of the first head, each
-        # against its full causal prefix, priced by the pairs they cover
-        import numpy as np
-
+        # long sequences: the dense oracle is far too slow for a whole head, so
+        # evenly spaced query rows of the first head, each against its full
+        # causal prefix, timed and priced by the pairs they cover; the rate is
+        # extrapolated from that sample to the whole workload
         sl = lambda t: t[0, 0].cpu()
         pairs = 0
-        for r in np.linspace(0, w.N - 1, 64).astype(np.int64):
-            O.forward_rows(sl(x["q1"]), sl(x["k1"]), sl(x["q2"]), sl(x["k2"]), sl(x["v"]), [int(r)], lam,
-                           x["lambda_init"], eps=x["eps"], causal=w.causal)
+        h = {k: sl(x[k]) for k in ("q1", "k1", "q2", "k2", "v")}
+        t0 = time.perf_counter()
+        for r in np.linspace(0, w.N - 1, 4096).astype(np.int64):
+            O.forward_rows(h["q1"], h["k1"], h["q2"], h["k2"], h["v"], [int(r)], lam, x["lambda_init"],
+                           eps=x["eps"], causal=w.causal)
             pairs += int(r) + 1 if w.causal else w.N
             done += 1
             if time.perf_counter() - t0 >= budget_s:
@@ -125,8 +188,10 @@ def cpu_baseline(x, w, budget_s: float):
         dt = time.perf_counter() - t0
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
         return {"value": 12.0 * w.d * pairs / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-                "kind": "oracle", "sample": f"{done} evenly spaced query rows of one head with their full "
-                                            f"causal prefixes, fp64 NumPy, {dt:.1f} s wall"}
+                "kind": "oracle", "extrapolated": True,
+                "sample": f"{done} evenly spaced query rows of head 0 with their full causal prefixes "
+                          f"({pairs} pairs of the workload's {w.pairs() * w.B * w.H}), fp64 NumPy, {dt:.1f} s "
+                          f"wall; rate extrapolated per pair"}
     for b, h in heads:
         sl = lambda t: t[b:b + 1, h:h + 1].cpu()
         O.forward(sl(x["q1"]), sl(x["k1"]), sl(x["q2"]), sl(x["k2"]), sl(x["v"]), lam, x["lambda_init"],
@@ -378,6 +443,8 @@ def main():
     ap.add_argument("--prefill-workload", default=None,
                     help="prefill workload to time instead of the headline one (a name in workloads.WORKLOADS)")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode leg")
+    ap.add_argument("--no-sublegs", action="store_true", help="skip the 1.4B / 3B layer prefill legs")
+    ap.add_argument("--sub-steps", type=int, default=40, help="timed steps of each layer prefill leg")
     ap.add_argument("--no-bwd", action="store_true", help="skip the training (backward) leg")
     ap.add_argument("--bwd-steps", type=int, default=40)
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 query/key prefill leg")
@@ -411,77 +478,36 @@ def main():
     if w.kind != "prefill" or w.dtype != "bf16":
         raise SystemExit(f"{w.name}: the prefill leg times bf16 prefill workloads")
     x = W.workload_inputs(w.name, device=dev)
-    lam_t = torch.empty(1, device=dev, dtype=torch.float32)
-    out = torch.empty_like(x["v"])
-
-    def step():
-        da.lam(x["lq1"], x["lk1"], x["lq2"], x["lk2"], x["lambda_init"], out=lam_t)
-        fwd()
-
-    def fwd():
-        da.fwd(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam_t, x["lambda_init"], eps=x["eps"],
-               causal=w.causal, out=out)
-
-    # The steps are replayed from a HIP graph so that the host's per-call
-    # overhead does not leave the GPU idle between launches: one graph holds
-    # R consecutive steps (each exactly the eager step's two library
-    # launches), replayed steps / R times, so one host launch covers R steps.
-    R = next(r for r in (20, 10, 8, 5, 4, 2, 1) if args.steps % r == 0)
-    step()
-    torch.cuda.synchronize()
-    eager = out.clone()
-
-    def steps_r():
-        for _ in range(R):
-            step()
-
-    def lams_r():
-        for _ in range(R):
-            da.lam(x["lq1"], x["lk1"], x["lq2"], x["lk2"], x["lambda_init"], out=lam_t)
-
-    g_step = _graph(steps_r, torch)
-    g_lam = _graph(lams_r, torch)
-    _prewarm(g_step.replay, args.prewarm_s, torch)
-    for _ in range(-(-args.warmup // R)):
-        g_step.replay()
-    total_ms = _timed(g_step.replay, args.steps // R, stream, torch)
-    if not torch.equal(out, eager):
-        raise RuntimeError("graph replay of the step differs from the eager step")
-    # The dominant kernel's own time in the same launch configuration: the
-    # step less its lambda launch, timed alone the same way.  (Forward
-    # launches replayed back to back with nothing between them run slower:
-    # each persistent grid then starts on compute units as the previous one
-    # releases them, unevenly.)
-    for _ in range(-(-args.warmup // R)):
-        g_lam.replay()
-    lam_ms = _timed(g_lam.replay, args.steps // R, stream, torch) / args.steps
-    kern_ms = total_ms / args.steps - lam_ms
-    ms_step = total_ms / args.steps
-    flops = 12.0 * w.d * w.pairs() * w.B * w.H
-    value = flops / (ms_step * 1e-3) / 1e12
-    achieved = flops / (kern_ms * 1e-3) / 1e12
+    leg, lam_ms = prefill_leg(w, x, args.steps, args.warmup, args.prewarm_s, stream, torch, da, W)
     res = {
-        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "prewarm_s": args.prewarm_s, "steps_per_graph": R,
-        "ms_per_step": round(ms_step, 4),
+        "metric": METRIC, "value": leg["value"], "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "prewarm_s": args.prewarm_s,
+        "steps_per_graph": leg["steps_per_graph"], "ms_per_step": leg["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         # the same step priced at Eq. 1's 8 d flops per pair (two PV products only)
-        "eq1_tflops": round(value * 8.0 / 12.0, 2),
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "v_width": 2 * w.d,
-                   "causal": w.causal, "lambda_init": x["lambda_init"],
-                   "flops_per_pair": 12 * w.d, "pairs_per_head": w.pairs()},
-        "roofline": {"bound": "mfma", "kernel": f"prefill_bf16_kernel<{w.d},{'causal' if w.causal else 'full'},norm>",
-                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": (_traffic("prefill_layer1p4b", "prefill.hip")
-                                 if w.name == W.HEADLINE_PREFILL else None),
-                     "kernel_ms": round(kern_ms, 4), "lambda_ms": round(lam_ms, 4)},
+        "eq1_tflops": round(leg["value"] * 8.0 / 12.0, 2),
+        "config": leg["config"],
+        "roofline": leg["roofline"],
     }
+    # cpu_baseline: the oracle on a bounded sample of the same workload
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(x, w, args.cpu_budget)
+    del x
+
+    # ---------------- the two model-layer prefills, each with its own roofline
+    if not args.prefill_workload and not args.no_sublegs:
+        res["prefill_layers"] = {}
+        for name in W.PREFILL_SUBLEGS:
+            ws = W.WORKLOADS[name]
+            xs = W.workload_inputs(name, device=dev)
+            sub, _ = prefill_leg(ws, xs, args.sub_steps, args.warmup, min(0.5, args.prewarm_s), stream, torch,
+                                 da, W)
+            res["prefill_layers"][name] = {k: sub[k] for k in ("ms_per_step", "value", "roofline", "config")}
+            del xs
 
     # ---------------- decode leg
     if not args.no_decode:
-        del out
         wd = W.WORKLOADS[W.HEADLINE_DECODE]
         y = W.workload_inputs(wd.name, device=dev)
         lam_d = da.lam(y["lq1"], y["lk1"], y["lq2"], y["lk2"], y["lambda_init"])
@@ -514,7 +540,8 @@ def main():
         # an error here must not cost the prefill and decode figures above:
         # it is reported in the leg's place (and on stderr)
         try:
-            res["backward"] = backward_leg(x, w, args, stream, torch, da)
+            wb = W.WORKLOADS["layer1p4b_bf16_b4h16n2048d64"]
+            res["backward"] = backward_leg(W.workload_inputs(wb.name, device=dev), wb, args, stream, torch, da)
         except Exception as e:  # noqa: BLE001
             print(f"training leg failed: {e!r}", file=sys.stderr, flush=True)
             res["backward"] = {"error": repr(e)}
@@ -541,6 +568,8 @@ def main():
             "what": "vendor bf16 GEMM 8192^3 (torch.matmul, hipBLASLt), sustained, same run; context only",
             "tflops": round(g, 1), "frac_of_peak": round(g / PEAK_BF16_TFLOPS, 4)}
         res["roofline"]["frac_of_reference_gemm"] = round(res["roofline"]["achieved"] / g, 4)
+        for sub in res.get("prefill_layers", {}).values():
+            sub["roofline"]["frac_of_reference_gemm"] = round(sub["roofline"]["achieved"] / g, 4)
 
     if args.copy_calib_mib > 0:
         n = args.copy_calib_mib * (1 << 20)
@@ -549,10 +578,6 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
         res["copy_calibration_bytes"] = n
-
-    # ---------------- CPU oracle on a bounded sample of the same workload
-    if not args.no_cpu:
-        res["cpu_baseline"] = cpu_baseline(x, w, args.cpu_budget)
 
     print(json.dumps(res), flush=True)
 

@@ -24,17 +24,30 @@ def test_more_than_one_gpu_is_refused_with_a_message():
 
 
 def test_traffic_only_for_the_source_it_was_taken_on(tmp_path, monkeypatch):
+    """The hash covers the kernel source and the headers it includes: a
+    change to either makes the stored traffic figure stale."""
     import bench
+    from transformer_attention_diffattn_amd import traffic_summary as ts
 
     prof = tmp_path / "profiles"
     prof.mkdir()
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
-    csrc = tmp_path / "transformer_attention_diffattn_amd" / "csrc"
+    pkg = tmp_path / "transformer_attention_diffattn_amd"
+    csrc = pkg / "csrc"
     csrc.mkdir(parents=True)
     (csrc / "k.hip").write_text("kernel source")
-    h = bench._src_hash("k.hip")
+    headers = tuple(str(csrc / n) for n in ("device_common.h", "kernels.h"))
+    for hp in headers:
+        open(hp, "w").write("header")
+    monkeypatch.setattr(ts, "PKG", str(pkg))
+    monkeypatch.setattr(ts, "HEADERS", headers)
+    h = ts.source_hash("k.hip")
     (prof / "x_traffic.json").write_text(json.dumps({"bytes_per_launch": 123, "source_sha256_16": h}))
     assert bench._traffic("x", "k.hip") == 123
     (csrc / "k.hip").write_text("changed kernel source")
+    assert bench._traffic("x", "k.hip") is None
+    (csrc / "k.hip").write_text("kernel source")
+    assert bench._traffic("x", "k.hip") == 123
+    open(headers[0], "w").write("changed helper")
     assert bench._traffic("x", "k.hip") is None
     assert bench._traffic("missing", "k.hip") is None

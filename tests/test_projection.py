@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 import torch
 
+from oracle import diffattn_oracle as O
 from oracle import projection_oracle as P
 from transformer_attention_diffattn_amd import binding as da
 from transformer_attention_diffattn_amd import workloads as W
@@ -105,17 +106,54 @@ def test_projections_full_size_3b_layer_sampled(dev):
            P.out_projection(_abs(os_), _abs(x["w_o"].cpu())), H * 2 * d)
 
 
-def test_layer_chain_runs_on_device_layouts(dev):
-    # in_proj -> diffattn_fwd -> out_proj with no copies between them: the
-    # projection outputs are the attention's inputs as they stand
-    B, N, dm, H, d = 1, 96, 256, 2, 64
+def test_layer_chain_parity_1p4b_slice(dev):
+    """in_proj -> lambda -> diffattn_fwd -> out_proj on the device layouts (no
+    copies between the calls) against projection_oracle then diffattn_oracle
+    then projection_oracle, all computed from x and the weights alone: a
+    slice of the 1.4B-scale layer (256 tokens, d_model 2048, 16 heads of
+    2d = 128).  Tutorial page "Differential attention", section "How it's
+    wired": the layer drops into the block in place of ordinary attention.
+
+    Composed bound, stage by stage against the fp64 chain:
+    * q1, k1, q2, k2, v: the projection bound above;
+    * attention output: the bf16 tolerance 2e-2 per element (it covers the
+      kernel's own rounding and the bf16 storage of its inputs, which moves
+      this output by under 8e-3 here);
+    * y: the attention errors e_c enter y_f = sum_c o_c W_O[f, c] as
+      independent per-channel errors of size at most 2e-2, so six standard
+      deviations give 6 * 2e-2 * ||W_O[f]||_2, plus the out-projection's own
+      rounding (the projection bound)."""
+    B, N, dm, H, d = 1, 256, 2048, 16, 64
+    lam_init = 0.8
     x = W.projection_inputs(B, N, dm, H, d, seed=31)
+    g = torch.Generator().manual_seed(32)
+    lv = [0.1 * torch.randn(d, generator=g) for _ in range(4)]
+    # device chain
     q1, k1, q2, k2, v = da.in_proj(x["x"].to(dev), x["w_qkv"].to(dev), H, d)
-    lam_t = torch.tensor([0.5], device=dev)
-    o = da.fwd(q1, k1, q2, k2, v, lam_t, 0.8)
+    lam_t = da.lam(*(t.to(dev) for t in lv), lam_init)
+    o = da.fwd(q1, k1, q2, k2, v, lam_t, lam_init)
     y = da.out_proj(o, x["w_o"].to(dev))
     torch.cuda.synchronize()
-    assert y.shape == (B, N, dm) and torch.isfinite(y.float()).all()
+    # oracle chain
+    ref_in = P.in_projection(x["x"], x["w_qkv"], H, d)
+    mag_in = P.in_projection(_abs(x["x"]), _abs(x["w_qkv"]), H, d)
+    for gt, r, m in zip((q1, k1, q2, k2, v), ref_in, mag_in):
+        _check(gt, r, m, dm)
+    lam = O.lambda_scalar(*lv, lam_init)
+    ref_o = O.forward(*ref_in, lam, lam_init)
+    err_o = float(np.max(np.abs(o.float().cpu().numpy() - ref_o)))
+    print(f"attention stage: max err {err_o:.3e} (bound 2e-2)", flush=True)
+    assert err_o <= 2e-2
+    ref_y = P.out_projection(ref_o, x["w_o"])
+    mag_y = P.out_projection(np.abs(ref_o), _abs(x["w_o"]))
+    wn = np.linalg.norm(x["w_o"].double().numpy(), axis=1)
+    K = H * 2 * d
+    tol = 6.0 * 2e-2 * wn + 2.0 ** -8 * np.abs(ref_y) + K * 2.0 ** -24 * (1 + 2.0 ** -8) * mag_y
+    err_y = np.abs(y.float().cpu().numpy() - ref_y)
+    worst = np.unravel_index(np.argmax(err_y / tol), err_y.shape)
+    print(f"output stage: max err {err_y.max():.3e}; worst vs bound {err_y[worst]:.3e} / {tol[worst]:.3e} "
+          f"(rms of y {np.sqrt(np.mean(ref_y ** 2)):.3e})", flush=True)
+    assert np.all(err_y <= tol)
 
 
 def test_projection_deterministic(dev):

@@ -15,8 +15,9 @@ The passes are runs of ``bench.py ... --copy-calib-mib M``, which also makes
 one device copy of M MiB.  FETCH_SIZE and WRITE_SIZE are in KiB per dispatch;
 each is scaled by the factor that makes the copy read and write exactly M MiB
 (the counters' own unit and sampling), then averaged over the kernel's
-dispatches.  The source hash lets ``bench.py`` report the figure only while
-the kernel source is the one the counters were taken on.
+dispatches.  The source hash (the kernel source and the headers it includes)
+lets ``bench.py`` report the figure only while the kernel is the one the
+counters were taken on.
 """
 
 from __future__ import annotations
@@ -28,6 +29,21 @@ import json
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
+# headers every kernel source includes: the MFMA, exp2, LDS-load and
+# buffer-store helpers, the launch interface and the ABI
+HEADERS = (os.path.join(PKG, "csrc", "device_common.h"), os.path.join(PKG, "csrc", "kernels.h"),
+           os.path.join(os.path.dirname(PKG), "include", "diffattn.h"))
+
+
+def source_hash(sources: str) -> str:
+    """Hash of the kernel sources (comma-separated names under csrc/) together
+    with the headers they include: a counter profile is current only while
+    this hash is unchanged."""
+    h = hashlib.sha256()
+    for path in [os.path.join(PKG, "csrc", n) for n in sources.split(",")] + list(HEADERS):
+        with open(path, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def _per_dispatch(path: str, pattern: str) -> list:
@@ -77,10 +93,6 @@ def main() -> None:
     if cf <= 0 or cw <= 0:
         raise SystemExit("no calibration copy found in the counter files")
     ff, fw = calib_kib / cf, calib_kib / cw
-    h = hashlib.sha256()
-    for n in a.source.split(","):
-        with open(os.path.join(PKG, "csrc", n), "rb") as fh:
-            h.update(fh.read())
     fetch_b, write_b = fetch_kib * ff * 1024, write_kib * fw * 1024
     out = {
         "kernel": " + ".join(a.kernel), "workload": a.workload, "dispatches": min(counts),
@@ -89,7 +101,7 @@ def main() -> None:
         "bytes_per_launch": int(round(fetch_b + write_b)),
         "fetch_bytes": int(round(fetch_b)), "write_bytes": int(round(write_b)),
         "algorithmic_bytes": a.algorithmic,
-        "source_sha256_16": h.hexdigest()[:16],
+        "source_sha256_16": source_hash(a.source),
     }
     print(json.dumps(out, indent=1))
 

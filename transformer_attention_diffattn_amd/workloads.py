@@ -68,9 +68,14 @@ WORKLOADS = {
     )
 }
 
-# the workload the headline prefill figure is quoted on, and the decode one
-HEADLINE_PREFILL = "layer1p4b_bf16_b4h16n2048d64"
+# the headline prefill workload: the largest prefill that fits one GPU (the
+# 64K-token context); the two model-layer prefills are reported beside it
+HEADLINE_PREFILL = "longctx_bf16_b1h12n65536d128"
+PREFILL_SUBLEGS = ("layer1p4b_bf16_b4h16n2048d64", "layer3b_bf16_b2h12n4096d128")
 HEADLINE_DECODE = "decode_bf16_b64h16l32768d128"
+# traffic summaries under profiles/ per prefill workload (prefill.hip counters)
+PREFILL_TRAFFIC = {"longctx_bf16_b1h12n65536d128": "prefill_longctx", "layer1p4b_bf16_b4h16n2048d64":
+                   "prefill_layer1p4b", "layer3b_bf16_b2h12n4096d128": "prefill_layer3b"}
 
 
 def _gen(seed: int, device) -> torch.Generator:
