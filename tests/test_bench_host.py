@@ -24,8 +24,9 @@ def test_more_than_one_gpu_is_refused_with_a_message():
 
 
 def test_traffic_only_for_the_source_it_was_taken_on(tmp_path, monkeypatch):
-    """The hash covers the kernel source and the headers it includes: a
-    change to either makes the stored traffic figure stale."""
+    """The hash covers the kernel source and the headers it includes (found
+    through its #include lines, recursively): a change to either makes the
+    stored traffic figure stale; a header it does not include does not."""
     import bench
     from transformer_attention_diffattn_amd import traffic_summary as ts
 
@@ -35,19 +36,20 @@ def test_traffic_only_for_the_source_it_was_taken_on(tmp_path, monkeypatch):
     pkg = tmp_path / "transformer_attention_diffattn_amd"
     csrc = pkg / "csrc"
     csrc.mkdir(parents=True)
-    (csrc / "k.hip").write_text("kernel source")
-    headers = tuple(str(csrc / n) for n in ("device_common.h", "kernels.h"))
-    for hp in headers:
-        open(hp, "w").write("header")
+    (csrc / "k.hip").write_text('#include "a.h"\nkernel source\n')
+    (csrc / "a.h").write_text('#include "b.h"\nhelper\n')
+    (csrc / "b.h").write_text("nested helper\n")
+    (csrc / "other.h").write_text("not included\n")
     monkeypatch.setattr(ts, "PKG", str(pkg))
-    monkeypatch.setattr(ts, "HEADERS", headers)
     h = ts.source_hash("k.hip")
     (prof / "x_traffic.json").write_text(json.dumps({"bytes_per_launch": 123, "source_sha256_16": h}))
     assert bench._traffic("x", "k.hip") == 123
-    (csrc / "k.hip").write_text("changed kernel source")
-    assert bench._traffic("x", "k.hip") is None
-    (csrc / "k.hip").write_text("kernel source")
+    (csrc / "other.h").write_text("changed, still not included\n")
     assert bench._traffic("x", "k.hip") == 123
-    open(headers[0], "w").write("changed helper")
+    (csrc / "b.h").write_text("changed nested helper\n")
+    assert bench._traffic("x", "k.hip") is None
+    (csrc / "b.h").write_text("nested helper\n")
+    assert bench._traffic("x", "k.hip") == 123
+    (csrc / "k.hip").write_text('#include "a.h"\nchanged kernel source\n')
     assert bench._traffic("x", "k.hip") is None
     assert bench._traffic("missing", "k.hip") is None

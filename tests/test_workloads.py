@@ -33,8 +33,15 @@ def test_needle_adds_exact_logit_boost():
 
 
 def test_workload_table_shapes():
+    # the headline prefill is the largest one that fits a GPU: the 64K context
     w = W.WORKLOADS[W.HEADLINE_PREFILL]
+    assert (w.B, w.H, w.N, w.d, w.dtype) == (1, 12, 65536, 128, "bf16")
+    assert w.pairs() == 65536 * 65537 // 2
+    big = max((v for v in W.WORKLOADS.values() if v.kind == "prefill"), key=lambda v: v.pairs() * v.B * v.H * v.d)
+    assert big.name == W.HEADLINE_PREFILL
+    w = W.WORKLOADS[W.PREFILL_SUBLEGS[0]]
     assert (w.B, w.H, w.N, w.d, w.dtype) == (4, 16, 2048, 64, "bf16")
     assert w.pairs() == 2048 * 2049 // 2
+    assert set(W.PREFILL_TRAFFIC) == {W.HEADLINE_PREFILL, *W.PREFILL_SUBLEGS}
     x = W.workload_inputs("tiny_fp32_b1h1n128d16")
     assert x["q1"].dtype == torch.float32 and x["v"].shape == (1, 1, 128, 32)

@@ -27,20 +27,35 @@ import csv
 import hashlib
 import json
 import os
+import re
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-# headers every kernel source includes: the MFMA, exp2, LDS-load and
-# buffer-store helpers, the launch interface and the ABI
-HEADERS = (os.path.join(PKG, "csrc", "device_common.h"), os.path.join(PKG, "csrc", "kernels.h"),
-           os.path.join(os.path.dirname(PKG), "include", "diffattn.h"))
+
+
+def _with_includes(path: str, seen: list) -> list:
+    """path and every header it includes with #include "..." (resolved next
+    to the including file), depth first, each once."""
+    path = os.path.normpath(path)
+    if path in seen:
+        return seen
+    seen.append(path)
+    with open(path) as fh:
+        for line in fh:
+            m = re.match(r'\s*#\s*include\s+"([^"]+)"', line)
+            if m:
+                _with_includes(os.path.join(os.path.dirname(path), m.group(1)), seen)
+    return seen
 
 
 def source_hash(sources: str) -> str:
     """Hash of the kernel sources (comma-separated names under csrc/) together
     with the headers they include: a counter profile is current only while
     this hash is unchanged."""
+    files: list = []
+    for n in sources.split(","):
+        _with_includes(os.path.join(PKG, "csrc", n), files)
     h = hashlib.sha256()
-    for path in [os.path.join(PKG, "csrc", n) for n in sources.split(",")] + list(HEADERS):
+    for path in files:
         with open(path, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
