@@ -138,6 +138,30 @@ DIFFATTN_API diffattn_status diffattn_decode(diffattn_dtype dt, const void* q1, 
                                 float eps, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * diffattn_decode_noalloc -- diffattn_decode without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  Same arguments,
+ * results (bit for bit) and errors as diffattn_decode; the split records go
+ * to a fixed device array inside the library, DIFFATTN_NOALLOC_SCRATCH_BYTES
+ * bytes, one per GPU, held until the process ends.  The call allocates
+ * nothing.
+ *   Sizes whose diffattn_decode_workspace_bytes(B, H, L_max, d) exceeds
+ *   DIFFATTN_NOALLOC_SCRATCH_BYTES return DIFFATTN_EWORKSPACE and launch
+ *   nothing (64 sequences x 16 heads x 32768 keys at d = 128 need 16.9 MB).
+ *   Every call on one GPU uses the same array: calls that overlap in time on
+ *   one GPU (different streams, or different host threads without ordering)
+ *   race and must not be issued; calls ordered on one stream are safe.
+ *   The first call on each device looks the array's address up (no
+ *   allocation); a failure there returns DIFFATTN_EHIP.
+ */
+#define DIFFATTN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+DIFFATTN_API diffattn_status diffattn_decode_noalloc(diffattn_dtype dt, const void* q1, const void* q2,
+                                        const void* k1c, const void* k2c, const void* vc,
+                                        const int* cache_len, void* out, int B, int H, int L_max,
+                                        int d, const float* lambda, float lambda_init,
+                                        const float* norm_weight, float eps, void* stream);
+
+/*
  * Training: the gradients of the same forward.  The review page's "Summary"
  * describes the layer as trained end to end (lambda through its vectors,
  * Eq. 2; the per-head normalisation of Eq. 3); the derivatives follow from

@@ -36,7 +36,7 @@ def L():
 def test_header_declares_the_abi():
     assert declared_symbols() == sorted([
         "diffattn_abi_version", "diffattn_bwd", "diffattn_bwd_workspace_bytes", "diffattn_decode",
-        "diffattn_decode_workspace_bytes", "diffattn_fwd", "diffattn_fwd_fp8qk", "diffattn_fwd_train",
+        "diffattn_decode_noalloc", "diffattn_decode_workspace_bytes", "diffattn_fwd", "diffattn_fwd_fp8qk", "diffattn_fwd_train",
         "diffattn_in_proj", "diffattn_lambda", "diffattn_lambda_bwd", "diffattn_out_proj", "diffattn_quantize_fp8", "diffattn_quantize_fp8_batch", "diffattn_quantize_fp8_workspace_bytes",
         "diffattn_strerror"])
 
@@ -143,6 +143,32 @@ def test_decode_validation(L):
         assert _dec(L, ptrs=p) == b.EINVAL
     assert _dec(L, B=0) == b.OK
     assert _dec(L, B=70000) == b.EINVAL
+
+
+def _dec_na(L, dt=b.BF16, d=128, B=2, H=2, Lmax=64, lens=None, ptrs=(A16,) * 6, eps=1e-5):
+    q1, q2, k1, k2, v, out = ptrs
+    return L.diffattn_decode_noalloc(dt, q1, q2, k1, k2, v, lens, out, B, H, Lmax, d, A16, 0.8, None, eps, None)
+
+
+def test_decode_noalloc_validation(L):
+    """The allocation-free decode validates like diffattn_decode and refuses,
+    before any HIP call, sizes whose split records exceed its fixed scratch."""
+    assert _dec_na(L, dt=3) == b.EUNSUPPORTED
+    assert _dec_na(L, d=100) == b.EUNSUPPORTED
+    assert _dec_na(L, Lmax=-1) == b.EINVAL
+    assert _dec_na(L, eps=-1e-3) == b.EINVAL
+    assert _dec_na(L, lens=A16 + 2) == b.EINVAL
+    for i in range(6):
+        p = [A16] * 6
+        p[i] = MIS
+        assert _dec_na(L, ptrs=p) == b.EINVAL
+    assert _dec_na(L, B=0) == b.OK
+    assert _dec_na(L, B=70000) == b.EINVAL
+    # 512 x 64 one-key caches: 32768 records of 2064 bytes > 32 MiB
+    assert L.diffattn_decode_workspace_bytes(512, 64, 1, 128) > b.NOALLOC_SCRATCH_BYTES
+    assert _dec_na(L, B=512, H=64, Lmax=1) == b.EWORKSPACE
+    # the benchmarked decode (64 x 16 x 32768 keys) fits
+    assert L.diffattn_decode_workspace_bytes(64, 16, 32768, 128) <= b.NOALLOC_SCRATCH_BYTES
 
 
 def _fwd_train(L, dt=b.BF16, d=64, B=1, H=1, N=8, flags=b.CAUSAL, lse=A16, o12=A16, ptrs=(A16,) * 6):

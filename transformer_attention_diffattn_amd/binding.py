@@ -42,6 +42,8 @@ def lib() -> ctypes.CDLL:
         L.diffattn_decode_workspace_bytes.restype = sz
         L.diffattn_decode.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, vp, f, vp, f, vp, sz, vp]
         L.diffattn_decode.restype = i
+        L.diffattn_decode_noalloc.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, vp, f, vp, f, vp]
+        L.diffattn_decode_noalloc.restype = i
         L.diffattn_strerror.argtypes = [i]
         L.diffattn_strerror.restype = ctypes.c_char_p
         L.diffattn_fwd_train.argtypes = [i, vp, vp, vp, vp, vp, vp, i, i, i, i, vp, f, vp, f, u, vp, vp, vp]
@@ -198,6 +200,46 @@ def decode(q1, q2, k1c, k2c, vc, lam_t, lambda_init: float, cache_len=None, weig
                                  _ptr(cache_len), _ptr(out), B, H, L, d, _ptr(lam_t), float(lambda_init),
                                  _ptr(weight), float(eps), _ptr(workspace), ws_bytes,
                                  _stream(q1.device)), "diffattn_decode")
+    return out
+
+
+# bytes of the library's fixed scratch array used by decode_noalloc
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def decode_noalloc(q1, q2, k1c, k2c, vc, lam_t, lambda_init: float, out, cache_len=None, weight=None,
+                   eps: float = 1e-5) -> torch.Tensor:
+    """``decode`` through diffattn_decode_noalloc: no workspace, the split
+    records go to the library's fixed device array (NOALLOC_SCRATCH_BYTES per
+    GPU), so the call allocates nothing; ``out`` [B,H,1,2d] is required.
+    Calls that overlap in time on one GPU share that array and must not be
+    issued."""
+    for n, t in (("q1", q1), ("q2", q2), ("k1c", k1c), ("k2c", k2c), ("vc", vc), ("lambda", lam_t)):
+        _dev(t, n)
+    if q1.dtype not in _DT:
+        raise ValueError("dtype must be float32 or bfloat16")
+    B, H, one, d = q1.shape
+    L = k1c.shape[2]
+    if one != 1 or q2.shape != q1.shape:
+        raise ValueError("q1/q2 must be [B,H,1,d]")
+    if k1c.shape != (B, H, L, d) or k2c.shape != (B, H, L, d) or vc.shape != (B, H, L, 2 * d):
+        raise ValueError("caches must be [B,H,L,d] and [B,H,L,2d]")
+    for t in (q2, k1c, k2c, vc):
+        if t.dtype != q1.dtype:
+            raise ValueError("all of q/k/v must share one dtype")
+    if cache_len is not None:
+        _dev(cache_len, "cache_len")
+        if cache_len.dtype != torch.int32 or cache_len.shape != (B,):
+            raise ValueError("cache_len must be int32 [B]")
+    _weight(weight, d)
+    _like(out, "out", (B, H, 1, 2 * d), q1.dtype, q1.device)
+    need = decode_workspace_bytes(B, H, L, d)
+    if need > NOALLOC_SCRATCH_BYTES:
+        raise ValueError(f"these sizes need {need} bytes of split records, more than the "
+                         f"{NOALLOC_SCRATCH_BYTES}-byte scratch of diffattn_decode_noalloc: use decode()")
+    _check(lib().diffattn_decode_noalloc(_DT[q1.dtype], _ptr(q1), _ptr(q2), _ptr(k1c), _ptr(k2c), _ptr(vc),
+                                         _ptr(cache_len), _ptr(out), B, H, L, d, _ptr(lam_t), float(lambda_init),
+                                         _ptr(weight), float(eps), _stream(q1.device)), "diffattn_decode_noalloc")
     return out
 
 

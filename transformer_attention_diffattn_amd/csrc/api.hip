@@ -38,6 +38,12 @@ hipError_t launch_lambda(const float* lq1, const float* lk1, const float* lq2, c
 
 }  // namespace diffattn
 
+namespace diffattn {
+// decode.hip: address of the allocation-free decode's fixed scratch array
+// (DIFFATTN_NOALLOC_SCRATCH_BYTES) on the device that runs `stream`
+hipError_t decode_scratch(hipStream_t stream, float** ptr);
+}  // namespace diffattn
+
 namespace {
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
@@ -342,43 +348,76 @@ size_t diffattn_decode_workspace_bytes(int B, int H, int L_max, int d) {
   return (size_t)B * H * S * diffattn::decode_record_floats(d) * sizeof(float);
 }
 
-diffattn_status diffattn_decode(diffattn_dtype dt, const void* q1, const void* q2, const void* k1c, const void* k2c,
-                                const void* vc, const int* cache_len, void* out, int B, int H, int L_max, int d,
-                                const float* lambda, float lambda_init, const float* norm_weight, float eps,
-                                void* workspace, size_t workspace_bytes, void* stream) {
+// validation and arguments shared by the two decode entry points (without
+// the workspace)
+static diffattn_status decode_args(diffattn_dtype dt, const void* q1, const void* q2, const void* k1c,
+                                   const void* k2c, const void* vc, const int* cache_len, void* out, int B, int H,
+                                   int L_max, int d, const float* lambda, float lambda_init,
+                                   const float* norm_weight, float eps, diffattn::DecodeArgs* a, bool* empty) {
+  *empty = false;
   if (dt != DIFFATTN_FP32 && dt != DIFFATTN_BF16) return DIFFATTN_EUNSUPPORTED;
   if (!supported_d(d)) return DIFFATTN_EUNSUPPORTED;
   if (B < 0 || H < 0 || L_max < 0) return DIFFATTN_EINVAL;
   if (!finite_nonneg(eps) || !isfinite(lambda_init)) return DIFFATTN_EINVAL;
-  if ((long long)B * H == 0) return DIFFATTN_OK;  // empty work: pointers are not inspected
+  if ((long long)B * H == 0) {  // empty work: pointers are not inspected
+    *empty = true;
+    return DIFFATTN_OK;
+  }
   if (B > 65535 || H > 65535) return DIFFATTN_EINVAL;
   if (!ok_ptr16(q1) || !ok_ptr16(q2) || !ok_ptr16(out) || !ok_ptr4(lambda)) return DIFFATTN_EINVAL;
   if (L_max > 0 && (!ok_ptr16(k1c) || !ok_ptr16(k2c) || !ok_ptr16(vc))) return DIFFATTN_EINVAL;
   if (cache_len && !aligned(cache_len, 4)) return DIFFATTN_EINVAL;
   if (norm_weight && !aligned(norm_weight, 4)) return DIFFATTN_EINVAL;
+  a->q1 = q1;
+  a->q2 = q2;
+  a->k1c = k1c;
+  a->k2c = k2c;
+  a->vc = vc;
+  a->cache_len = cache_len;
+  a->out = out;
+  a->B = B;
+  a->H = H;
+  a->L = L_max;
+  diffattn::decode_plan(B, H, L_max, d, &a->S, &a->chunk);
+  a->lambda = lambda;
+  a->out_scale = 1.0f - lambda_init;
+  a->norm_w = norm_weight;
+  a->eps = eps;
+  a->c = (float)(1.4426950408889634 / sqrt((double)d));
+  a->ws = nullptr;
+  return DIFFATTN_OK;
+}
+
+diffattn_status diffattn_decode(diffattn_dtype dt, const void* q1, const void* q2, const void* k1c, const void* k2c,
+                                const void* vc, const int* cache_len, void* out, int B, int H, int L_max, int d,
+                                const float* lambda, float lambda_init, const float* norm_weight, float eps,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  diffattn::DecodeArgs a;
+  bool empty = false;
+  const diffattn_status st = decode_args(dt, q1, q2, k1c, k2c, vc, cache_len, out, B, H, L_max, d, lambda,
+                                         lambda_init, norm_weight, eps, &a, &empty);
+  if (st != DIFFATTN_OK || empty) return st;
   const size_t need = diffattn_decode_workspace_bytes(B, H, L_max, d);
   if (workspace == nullptr || workspace_bytes < need) return DIFFATTN_EWORKSPACE;
   if (!aligned(workspace, 16)) return DIFFATTN_EINVAL;
-
-  diffattn::DecodeArgs a;
-  a.q1 = q1;
-  a.q2 = q2;
-  a.k1c = k1c;
-  a.k2c = k2c;
-  a.vc = vc;
-  a.cache_len = cache_len;
-  a.out = out;
-  a.B = B;
-  a.H = H;
-  a.L = L_max;
-  diffattn::decode_plan(B, H, L_max, d, &a.S, &a.chunk);
-  a.lambda = lambda;
-  a.out_scale = 1.0f - lambda_init;
-  a.norm_w = norm_weight;
-  a.eps = eps;
-  a.c = (float)(1.4426950408889634 / sqrt((double)d));
   a.ws = (float*)workspace;
   hipError_t e = diffattn::launch_decode(dt == DIFFATTN_BF16, d, true, a, (hipStream_t)stream);
+  return e == hipSuccess ? DIFFATTN_OK : DIFFATTN_EHIP;
+}
+
+diffattn_status diffattn_decode_noalloc(diffattn_dtype dt, const void* q1, const void* q2, const void* k1c,
+                                        const void* k2c, const void* vc, const int* cache_len, void* out, int B,
+                                        int H, int L_max, int d, const float* lambda, float lambda_init,
+                                        const float* norm_weight, float eps, void* stream) {
+  diffattn::DecodeArgs a;
+  bool empty = false;
+  const diffattn_status st = decode_args(dt, q1, q2, k1c, k2c, vc, cache_len, out, B, H, L_max, d, lambda,
+                                         lambda_init, norm_weight, eps, &a, &empty);
+  if (st != DIFFATTN_OK || empty) return st;
+  if (diffattn_decode_workspace_bytes(B, H, L_max, d) > DIFFATTN_NOALLOC_SCRATCH_BYTES) return DIFFATTN_EWORKSPACE;
+  hipError_t e = diffattn::decode_scratch((hipStream_t)stream, &a.ws);
+  if (e != hipSuccess) return DIFFATTN_EHIP;
+  e = diffattn::launch_decode(dt == DIFFATTN_BF16, d, true, a, (hipStream_t)stream);
   return e == hipSuccess ? DIFFATTN_OK : DIFFATTN_EHIP;
 }
 

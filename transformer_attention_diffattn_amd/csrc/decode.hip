@@ -19,6 +19,9 @@
 //     shuffle reductions of the maxima and denominators, a fixed split order
 //     for the numerators), then forms Y and applies the epilogue.
 
+#include <mutex>
+
+#include "../../include/diffattn.h"
 #include "device_common.h"
 #include "kernels.h"
 
@@ -304,6 +307,45 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Scratch of the allocation-free entry point: the split records of one call
+// (B*H*S records of 4 + 4d floats).  Every split writes its whole record
+// before the merge reads it, so the array never needs clearing; calls that
+// overlap on one GPU share it and race.
+
+static __device__ __align__(256) unsigned char scratch[DIFFATTN_NOALLOC_SCRATCH_BYTES];
+
+// The array's address on the device that runs `stream`, looked up once per
+// device with that device current (the host-side name is only a stand-in
+// and never reaches a kernel).  No allocation happens.
+hipError_t decode_scratch(hipStream_t stream, float** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  int dev = cur;
+  if (stream != nullptr) {
+    e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return e;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = (float*)addr[dev];
+  return hipSuccess;
+}
 
 void decode_plan(int B, int H, int L, int d, int* S, int* chunk) {
   (void)d;
