@@ -187,7 +187,9 @@ __device__ __forceinline__ i32x8 cat_i32x8(u32x4 lo, u32x4 hi) {
 
 // SAVE: the training forward (also writes the per-map statistics).
 // F8: e4m3 queries and keys with per-tensor scales (a.qk_scale).
-template <int D, bool CAUSAL, bool NORM, bool SAVE, bool F8>
+// XCD: the per-XCD schedule of long sequences (see the schedule below; the
+// host picks it when its conditions hold).
+template <int D, bool CAUSAL, bool NORM, bool SAVE, bool F8, bool XCD = false>
 __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(PrefillArgs a) {
   using T = Bf16Tile<D, F8>;
   using QFrag = std::conditional_t<F8, i32x8, bf16x8>;
@@ -220,13 +222,39 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
   // that every workgroup's total is about the same.  When G is a multiple of
   // B*H only the tile order is reversed, keeping each head on one workgroup
   // position (and so on one XCD's L2).
+  //   Long sequences (XCD: a multiple of, and at least four, chunks of W =
+  // G/8 query tiles per head) are grouped per XCD instead: workgroups are dealt
+  // to the 8 XCDs round robin (g % 8), and in each round the W workgroups of
+  // one XCD take the W query tiles of one chunk of ONE head, so they stream
+  // the same key tiles through that XCD's L2 at about the same time (rather
+  // than each L2 serving the key streams of several heads).  Chunks go
+  // longest first, heads fastest, chunk c of the order to XCD c % 8 in round
+  // c / 8; within a chunk workgroup j takes tile j, or W-1-j in odd rounds,
+  // so that the totals of an XCD's workgroups even out.
   const int G = gridDim.x, g = blockIdx.x, BH = a.BH;
   const int n_items = a.n_qtiles * BH;  // below 2^31 (checked by the host)
   auto item_at = [&](int r) -> int {
-    // integer division expands to vector code: keep the result scalar
-    const int alt = __builtin_amdgcn_readfirstlane((G % BH == 0) ? ((G / BH - 1 - g / BH) * BH + g % BH) : (G - 1 - g));
-    const int i = r * G + ((r & 1) ? alt : g);
-    return __builtin_amdgcn_readfirstlane(i < n_items ? i : -1);
+    if constexpr (XCD) {
+      constexpr int NXCD = 8;
+      const int W = G / NXCD;
+      // c / BH without the vector code of an integer division: a multiply
+      // by ceil(2^32 / BH) in scalar registers, corrected by one either way
+      const uint32_t inv_bh = __builtin_amdgcn_readfirstlane((uint32_t)(0xffffffffu / (uint32_t)BH) + 1u);
+      const int c = r * NXCD + g % NXCD;  // chunk
+      if (c >= n_items / W) return -1;
+      int kk = (int)__umulhi((uint32_t)c, inv_bh);
+      kk -= kk * BH > c ? 1 : 0;
+      kk += (kk + 1) * BH <= c ? 1 : 0;
+      kk = __builtin_amdgcn_readfirstlane(kk);
+      const int j = g / NXCD;
+      const int qi = kk * W + ((r & 1) ? W - 1 - j : j);
+      return __builtin_amdgcn_readfirstlane(qi * BH + (c - kk * BH));
+    } else {
+      // integer division expands to vector code: keep the result scalar
+      const int alt = __builtin_amdgcn_readfirstlane((G % BH == 0) ? ((G / BH - 1 - g / BH) * BH + g % BH) : (G - 1 - g));
+      const int i = r * G + ((r & 1) ? alt : g);
+      return __builtin_amdgcn_readfirstlane(i < n_items ? i : -1);
+    }
   };
 
   // One item; every field is wave-uniform and kept in scalar registers.
@@ -1180,6 +1208,17 @@ static hipError_t compute_units(int* ncu) {
   return e;
 }
 
+// The per-XCD schedule of long causal sequences: a grid of 8 equal XCD shares whose
+// W workgroups each take whole chunks of W query tiles of one head (at least
+// four chunks per head, so that chunk lengths differ little), unless the
+// grid is already a multiple of B*H (then each head keeps its workgroup
+// positions, and so its XCD, anyway).
+bool prefill_xcd_schedule(long long grid, int BH, int n_qtiles) {
+  if (grid % 8 != 0 || grid % BH == 0) return false;
+  const long long W = grid / 8;
+  return n_qtiles % W == 0 && n_qtiles >= 4 * W;
+}
+
 template <int D, bool C, bool NM, bool SV, bool F8 = false>
 static hipError_t launch_one(bool bf16, const PrefillArgs& a, hipStream_t s) {
   const long long items = (long long)a.n_qtiles * (long long)a.BH;
@@ -1190,7 +1229,12 @@ static hipError_t launch_one(bool bf16, const PrefillArgs& a, hipStream_t s) {
     const hipError_t e = compute_units(&ncu);
     if (e != hipSuccess) return e;
     const long long grid = items < ncu ? items : (ncu > 0 ? ncu : 1);
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, C, NM, SV, F8>), dim3((unsigned)grid), block, 0, s, a);
+    bool xcd = false;
+    if constexpr (C) xcd = prefill_xcd_schedule(grid, a.BH, a.n_qtiles);  // causal only
+    if (xcd)
+      hipLaunchKernelGGL((prefill_bf16_kernel<D, C, NM, SV, F8, C>), dim3((unsigned)grid), block, 0, s, a);
+    else
+      hipLaunchKernelGGL((prefill_bf16_kernel<D, C, NM, SV, F8, false>), dim3((unsigned)grid), block, 0, s, a);
   } else if constexpr (!SV && !F8) {
     hipLaunchKernelGGL((prefill_f32_kernel<D, C, NM>), dim3((unsigned)items), block, 0, s, a);
   } else {
