@@ -272,7 +272,7 @@ def proj_leg(args, stream, torch, da, W):
                     "vendor_gemm_tflops": round(f_in / (ms["vendor_in"] * 1e-3) / 1e12, 1)},
         "out_proj": {"ms": round(ms["out"], 4), "tflops": round(t_out, 1),
                      "vendor_gemm_tflops": round(f_out / (ms["vendor_out"] * 1e-3) / 1e12, 1)},
-        "roofline": {"bound": "mfma", "kernel": "proj_kernel<in-projection>", "achieved": round(t_in, 1),
+        "roofline": {"bound": "mfma", "kernel": "proj256_kernel<in-projection>", "achieved": round(t_in, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(t_in / PEAK_BF16_TFLOPS, 4),
                      "traffic": _traffic("proj_in_layer1p4b", "proj.hip"), "algorithmic_bytes": 159383552},
     }

@@ -69,6 +69,30 @@ def test_out_proj(dev, B, H, N, d, dout):
     _check(y, P.out_projection(x["o"], x["w_o"]), P.out_projection(_abs(x["o"]), _abs(x["w_o"])), H * 2 * d)
 
 
+# shapes large enough for the 256 x 256 large-tile form (reduction a multiple
+# of 64), with ragged token and feature edges and workgroups past the tile
+# grid: every element against the oracle
+@pytest.mark.parametrize("B,N,dm,H,d", [(1, 3000, 512, 8, 64), (2, 2100, 256, 6, 128)])
+def test_in_proj_large_tiles_ragged(dev, B, N, dm, H, d):
+    print(f"case in_proj large B={B} N={N} d_model={dm} H={H} d={d}", flush=True)
+    x = W.projection_inputs(B, N, dm, H, d, seed=970 + N)
+    outs = da.in_proj(x["x"].to(dev), x["w_qkv"].to(dev), H, d)
+    torch.cuda.synchronize()
+    ref = P.in_projection(x["x"], x["w_qkv"], H, d)
+    mag = P.in_projection(_abs(x["x"]), _abs(x["w_qkv"]), H, d)
+    for g, r, m in zip(outs, ref, mag):
+        _check(g, r, m, dm)
+
+
+@pytest.mark.parametrize("B,H,N,d,dout", [(1, 8, 8300, 32, 1000), (2, 4, 4150, 64, 1028)])
+def test_out_proj_large_tiles_ragged(dev, B, H, N, d, dout):
+    print(f"case out_proj large B={B} H={H} N={N} d={d} d_out={dout}", flush=True)
+    x = W.projection_inputs(B, N, 64, H, d, seed=990 + N, d_out=dout)
+    y = da.out_proj(x["o"].to(dev), x["w_o"].to(dev))
+    torch.cuda.synchronize()
+    _check(y, P.out_projection(x["o"], x["w_o"]), P.out_projection(_abs(x["o"]), _abs(x["w_o"])), H * 2 * d)
+
+
 def test_projections_full_size_1p4b_layer_sampled(dev):
     # the benchmarked shapes: 4 x 2048 tokens, d_model 2048, 16 heads of 2d = 128;
     # every output feature of sampled tokens against the oracle

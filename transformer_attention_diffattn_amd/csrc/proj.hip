@@ -197,9 +197,200 @@ __global__ __launch_bounds__(256, 2) void proj_kernel(ProjArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// The large-tile form (reduction length a multiple of 64; for the
+// out-projection a head width 2d of at least 64, so that a 64-wide step of
+// the reduction lies inside one head): a workgroup of 8 waves owns 256
+// features x 256 tokens, each wave 128 features x 64 tokens (8 x 4 MFMA
+// blocks), one workgroup per compute unit.  Operand tiles go from global
+// memory straight into LDS (global_load_lds_dwordx4, 1 KB = 8 rows of 64
+// reduction elements per instruction), double-buffered, 64 reduction
+// elements per step; each 128-byte row's eight 16-byte chunks are
+// XOR-swizzled by (row mod 8) on the global side, so that the eight rows of
+// each fragment read fall on distinct bank groups.  Per wave and step, 12
+// fragment reads (12 KB) feed 64 products: a quarter fewer LDS bytes per
+// product than the 128 x 128 form.
+//   Tile order: workgroups are dealt to the 8 XCDs round robin by launch
+// index; the tile grid is cut into blocks of 4 feature tiles x 8 token tiles,
+// block b going to XCD b % 8 as its (b / 8)-th round, so the 32 workgroups
+// that an XCD runs together share 1024 weight rows and 2048 token rows,
+// streamed through its L2 in step.
+
+constexpr int kBigTile = 256;
+constexpr int kBigFB = 4, kBigMB = 8;  // tiles per XCD block: features x tokens
+
+template <int MODE>
+__global__ __launch_bounds__(512, 1) void proj256_kernel(ProjArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lr = lane & 15, lg = lane >> 4;
+  const int K = a.K, F = a.F, M = a.M, N = a.N, H = a.H;
+  const int l2dv = a.log2_dv;
+  // tile order (see above); the grid covers whole rounds of 8 XCD blocks,
+  // and a workgroup whose block or tile lies past the tile grid has nothing
+  // to do (it leaves before any barrier)
+  const int nFt = (F + kBigTile - 1) / kBigTile, nMt = (M + kBigTile - 1) / kBigTile;
+  const int nFb = (nFt + kBigFB - 1) / kBigFB, nMb = (nMt + kBigMB - 1) / kBigMB;
+  const int L = blockIdx.x;
+  const int bi = (L % 8) + 8 * ((L / 8) / (kBigFB * kBigMB));  // XCD block
+  const int slot = (L / 8) % (kBigFB * kBigMB);
+  const int tile_f = (bi % nFb) * kBigFB + slot % kBigFB;
+  const int tile_m = (bi / nFb) * kBigMB + slot / kBigFB;
+  if (bi >= nFb * nMb || tile_f >= nFt || tile_m >= nMt) return;
+  const int wf0 = tile_f * kBigTile, wm0 = tile_m * kBigTile;
+  const int n0 = wf0 + (wave & 1) * 128;   // this wave's features
+  const int m0 = wm0 + (wave >> 1) * 64;   // this wave's tokens
+
+  // LDS: [buffer][W, X][256 rows][64] bf16 = 2 x 2 x 32 KB
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][kBigTile * 64];
+  const uint32_t lds0 = lds_offset(lds);
+  // Loads of one step: 32 instructions for the W tile and 32 for the X tile,
+  // 8 rows each; wave w issues W instructions w, w + 8, w + 16, w + 24 and
+  // the same X instructions.  Lane l fills LDS row 8 i + l / 8, physical
+  // chunk l % 8, which holds logical chunk (l % 8) ^ (row % 8).
+  const int prow = lane >> 3;
+  const int lchunk = (lane & 7) ^ (prow & 7);  // rows 8i + prow: row % 8 == prow
+  uint32_t woff[4];                    // byte offsets from the W tile's first row
+  const uint16_t* xrow[4];             // X rows (token m) at reduction index 0
+  size_t xh_stride = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int r = 8 * (wave + 8 * u) + prow;  // row within the tile
+    woff[u] = (uint32_t)(min(wf0 + r, F - 1) - wf0) * (uint32_t)K * 2u + 16u * (uint32_t)lchunk;
+    const int m = min(wm0 + r, M - 1);
+    if (MODE == 0) {
+      xrow[u] = (const uint16_t*)a.x + (size_t)m * K + 8 * lchunk;
+    } else {
+      const int b = m / N, t = m - b * N;
+      xrow[u] = (const uint16_t*)a.x + (((size_t)b * H * N + (size_t)t) << l2dv) + 8 * lchunk;
+    }
+  }
+  if (MODE == 1) xh_stride = (size_t)N << l2dv;
+  const uint16_t* wbase = (const uint16_t*)a.w + (size_t)wf0 * K;
+  auto issue = [&](int ks, int buf) {
+    const int k0 = 64 * ks;
+    const uint32_t lw = lds0 + (uint32_t)(buf * 2 * kBigTile * 64 * 2);
+    const uint32_t lx = lw + (uint32_t)(kBigTile * 64 * 2);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      lds_dma16_s(wbase, woff[u] + 2u * (uint32_t)k0, lw + 1024u * (uint32_t)(wave + 8 * u));
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint16_t* src;
+      if (MODE == 0)
+        src = xrow[u] + k0;
+      else
+        src = xrow[u] + (size_t)(k0 >> l2dv) * xh_stride + (k0 & ((1 << l2dv) - 1));
+      lds_dma16(src, lx + 1024u * (uint32_t)(wave + 8 * u));
+    }
+  };
+  // fragment of half s (k 32s .. 32s + 31): row `row` of a tile, chunk 4s + lg
+  auto frag = [&](const uint16_t* t, int row, int s) {
+    return as_bf16x8(*reinterpret_cast<const u32x4*>(t + row * 64 + 8 * ((4 * s + lg) ^ (row & 7))));
+  };
+
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = zero_f32x4();
+
+  const int nk = K / 64;
+  const int wr0 = (wave & 1) * 128, xr0 = (wave >> 1) * 64;
+  issue(0, 0);
+  for (int ks = 0; ks < nk; ++ks) {
+    const int buf = ks & 1;
+    // this wave's loads of step ks have landed; the barrier extends that to
+    // everybody's, and everybody is done reading the other buffer (step ks-1)
+    wait_vmem();
+    __syncthreads();
+    if (ks + 1 < nk) issue(ks + 1, buf ^ 1);
+    const uint16_t* tw = lds[buf][0];
+    const uint16_t* tx = lds[buf][1];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      bf16x8 bfr[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bfr[j] = frag(tx, xr0 + 16 * j + lr, s);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const bf16x8 af = frag(tw, wr0 + 16 * i + lr, s);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32_bf16(af, bfr[j], acc[i][j]);
+      }
+    }
+  }
+
+  // epilogue as in proj_kernel: lane holds features n0 + 16i + 4lg .. +3 of
+  // token m0 + 16j + lr
+  int tb[4], tt[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int m = min(m0 + 16 * j + lr, M - 1);
+    tb[j] = m / N;
+    tt[j] = m - tb[j] * N;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int n = n0 + 16 * i + 4 * lg;
+    if (n >= F) continue;
+    uint16_t* base = (uint16_t*)a.y;
+    int l2w = 0, h = 0, ch = n;
+    if (MODE == 0) {
+      const int width = H << l2dv;
+      const int part = n / width, r = n - part * width;
+      h = r >> l2dv;
+      const int c = r & ((1 << l2dv) - 1);
+      if (part == 2) {
+        base = (uint16_t*)a.v;
+        l2w = l2dv;
+        ch = c;
+      } else {
+        const int half = c >> (l2dv - 1);
+        base = (uint16_t*)(part == 0 ? (half ? a.q2 : a.q1) : (half ? a.k2 : a.k1));
+        l2w = l2dv - 1;
+        ch = c & ((1 << l2w) - 1);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int m = m0 + 16 * j + lr;
+      if (m >= M) continue;
+      const u32x2 pk = {pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3])};
+      size_t off;
+      if (MODE == 0)
+        off = ((((size_t)tb[j] * H + h) * N + (size_t)tt[j]) << l2w) + ch;
+      else
+        off = (size_t)m * F + n;
+      *reinterpret_cast<u32x2*>(base + off) = pk;
+    }
+  }
+}
+
 }  // namespace
 
+// The large-tile form needs a reduction length that is a multiple of 64 and
+// a head width of at least 64 when it reads the per-head attention output;
+// it pays for large products only (at least one full round of XCD blocks).
+// Its grid: whole rounds of 8 XCD blocks of 4 x 8 tiles of 256.
+static long long proj256_grid(int mode, const ProjArgs& a) {
+  if (a.K % 64 != 0 || (mode == 1 && a.log2_dv < 6)) return 0;
+  const long long nFt = (a.F + kBigTile - 1) / kBigTile, nMt = (a.M + kBigTile - 1) / kBigTile;
+  const long long blocks = ((nFt + kBigFB - 1) / kBigFB) * ((nMt + kBigMB - 1) / kBigMB);
+  if (nFt * nMt < 8LL * kBigFB * kBigMB / 2) return 0;
+  return (blocks + 7) / 8 * 8 * kBigFB * kBigMB;
+}
+
 hipError_t launch_proj(int mode, const ProjArgs& a, hipStream_t stream) {
+  const long long g256 = proj256_grid(mode, a);
+  if (g256 > 0) {
+    const unsigned grid = (unsigned)g256;
+    if (mode == 0)
+      hipLaunchKernelGGL(proj256_kernel<0>, dim3(grid), dim3(512), 0, stream, a);
+    else
+      hipLaunchKernelGGL(proj256_kernel<1>, dim3(grid), dim3(512), 0, stream, a);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)((a.F + kProjTile - 1) / kProjTile), (unsigned)((a.M + kProjTile - 1) / kProjTile));
   if (mode == 0)
     hipLaunchKernelGGL(proj_kernel<0>, grid, dim3(256), 0, stream, a);
