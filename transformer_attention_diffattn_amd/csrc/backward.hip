@@ -378,7 +378,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     const uint16_t* sk1 = stg + (kt % kStages) * STAGE;
     const uint16_t* sk2 = sk1 + BN * D;
     const uint16_t* sv = sk1 + 2 * BN * D;
-    if (qw >= N || (CAUSAL && k0 > qw + 16 * SUB - 1)) continue;  // nothing visible to this wave
+    // nothing visible to this wave: its dQ products still run, on zero dS,
+    // so that every path through the loop updates the accumulators in place
+    // (a path around them makes the compiler copy all of them every tile)
+    const bool skip = qw >= N || (CAUSAL && k0 > qw + 16 * SUB - 1);
 
     float g1[SUB][2][4], g2[SUB][2][4];
     // the tile holds keys past a row of this wave's diagonal, or keys or
@@ -424,10 +427,18 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       }
     };
     // (at d = 128 a second copy of the tile body would not fit the registers)
-    if (D >= 128 || masked)
+    if (skip) {
+#pragma unroll
+      for (int u = 0; u < SUB; ++u)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) g1[u][kb][j] = g2[u][kb][j] = 0.f;
+    } else if (D >= 128 || masked) {
       scores(std::true_type{});
-    else
+    } else {
       scores(std::false_type{});
+    }
     bf16x8 b1[SUB], b2[SUB];
 #pragma unroll
     for (int u = 0; u < SUB; ++u) {
