@@ -226,28 +226,39 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(BwdArgs a) {
   }
   if (lane == 0) sdl[wave] = dl;
   __syncthreads();
-  float* part = a.partial + (size_t)blockIdx.x * (DV + 1);
+  // partials stored column-major ([2d + 1][blocks]) so that the reduction
+  // reads each column contiguously
+  float* part = a.partial + blockIdx.x;
+  const size_t np = gridDim.x;
   for (int c = threadIdx.x; c < DV; c += kPrepThreads) {
     float s = 0.f;
 #pragma unroll
     for (int v = 0; v < WAVES; ++v) s += sdw[v][c];
-    part[c] = s;
+    part[(size_t)c * np] = s;
   }
   if (threadIdx.x == 0) {
     float s = 0.f;
 #pragma unroll
     for (int v = 0; v < WAVES; ++v) s += sdl[v];
-    part[DV] = s;
+    part[(size_t)DV * np] = s;
   }
 }
 
 // fixed-order sums of the per-workgroup partials, one wave per column:
-// dw [2d] (columns 0..2d-1) and dlambda (column 2d)
+// dw [2d] (columns 0..2d-1) and dlambda (column 2d); a column's nparts
+// values are contiguous, read 256 at a time (four independent sums per lane)
 __global__ __launch_bounds__(64) void bwd_reduce_kernel(const float* __restrict__ partial, int nparts, int width,
                                                         float* __restrict__ dweight, float* __restrict__ dlambda) {
   const int c = blockIdx.x;
-  float s = 0.f;
-  for (int p = threadIdx.x; p < nparts; p += 64) s += partial[(size_t)p * width + c];
+  const float* col = partial + (size_t)c * nparts;
+  float s4[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int p0 = 0; p0 < nparts; p0 += 256)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int p = p0 + 64 * k + threadIdx.x;
+      if (p < nparts) s4[k] += col[p];
+    }
+  float s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
   s = wave_sum(s);
   if (threadIdx.x == 0) {
     if (c == width - 1)
