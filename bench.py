@@ -380,6 +380,33 @@ def fp8_leg(args, stream, torch, da, W):
         ms[name] = _timed(g.replay, steps // R, stream, torch) / steps
     if not torch.equal(out8, eager):
         raise RuntimeError("graph replay of the fp8 prefill differs from the eager call")
+    # the layer step the fp8 path sits in: the in-projection (B*N tokens x
+    # d_model = H*2d -> Q1, K1, Q2, K2, V) then the attention, bf16 against
+    # quantise + fp8 attention, each chain replayed from graphs like the rest
+    p = W.projection_inputs(w.B, w.N, w.H * 2 * w.d, w.H, w.d, seed=w.seed + 11, device=dev)
+    pq = da.in_proj(p["x"], p["w_qkv"], w.H, w.d)
+    pcodes = [torch.empty(t.shape, dtype=torch.uint8, device=dev) for t in pq[:4]]
+    pscales = torch.empty(4, dtype=torch.float32, device=dev)
+
+    def proj():
+        da.in_proj(p["x"], p["w_qkv"], w.H, w.d, outs=pq)
+
+    def chain16():
+        proj()
+        da.fwd(pq[0], pq[1], pq[2], pq[3], pq[4], lam_t, x["lambda_init"], eps=x["eps"], causal=w.causal,
+               out=out16)
+
+    def chain8():
+        proj()
+        da.quantize_fp8_batch(list(pq[:4]), codes=pcodes, scales=pscales, workspace=qws)
+        da.fwd_fp8qk(pcodes[0], pcodes[1], pcodes[2], pcodes[3], pscales, pq[4], lam_t, x["lambda_init"],
+                     eps=x["eps"], causal=w.causal, out=out8)
+
+    for name, fn in (("proj", proj), ("chain16", chain16), ("chain8", chain8)):
+        g = _graph(lambda fn=fn: [fn() for _ in range(R)], torch)
+        _prewarm(g.replay, min(0.3, args.prewarm_s), torch)
+        ms[name] = _timed(g.replay, steps // R, stream, torch) / steps
+    del p, pq, pcodes
     flops = 12.0 * w.d * w.pairs() * w.B * w.H
     peak = 12.0 / (4.0 / PEAK_FP8_TFLOPS + 8.0 / PEAK_BF16_TFLOPS)
     achieved = flops / (ms["fp8"] * 1e-3) / 1e12
@@ -395,6 +422,11 @@ def fp8_leg(args, stream, torch, da, W):
                      "frac": round(achieved / peak, 4),
                      "traffic": _traffic("prefill_fp8qk_layer3b", "prefill.hip"),
                      "peak_mix": "QK^T 4 d flops/pair at fp8 5033.2, PV 8 d at bf16 2516.6 TFLOP/s"},
+        "layer_chain": {"what": "in-projection (%d tokens x %d -> %d) then attention" % (
+                            w.B * w.N, w.H * 2 * w.d, 3 * w.H * 2 * w.d),
+                        "in_proj_ms": round(ms["proj"], 4), "bf16_ms": round(ms["chain16"], 4),
+                        "fp8_ms": round(ms["chain8"], 4),
+                        "fp8_speedup": round(ms["chain16"] / ms["chain8"], 3)},
         "quantize": {"ms_per_call": round(ms["quant"], 4), "tensors": 4,
                      "end_to_end_ms": round(ms["quant"] + ms["fp8"], 4),
                      "roofline": {"bound": "hbm", "kernel": "amax_partial_kernel + quantize_kernel (4 tensors)",
