@@ -337,9 +337,10 @@ where dV and dK are also computed apart)."""
 
 def fp8_leg(args, stream, torch, da, W):
     """The fp8 query/key prefill (diffattn_fwd_fp8qk) against the bf16 prefill
-    on the same d = 128 workload, and the quantiser that feeds it.  Its peak
-    is that of its mix: per causal pair 4 d flops of QK^T at the fp8 rate and
-    8 d of PV at the bf16 rate."""
+    on the same d = 128 workload, the quantiser that feeds it, and the layer
+    step around it (in-projection, then either attention).  Its peak is that
+    of its mix: per causal pair 4 d flops of QK^T at the fp8 rate and 8 d of
+    PV at the bf16 rate."""
     w = W.WORKLOADS["layer3b_bf16_b2h12n4096d128"]
     dev = torch.device("cuda:0")
     x = W.workload_inputs(w.name, device=dev)
