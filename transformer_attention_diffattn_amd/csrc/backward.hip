@@ -646,7 +646,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdArgs a) {
         if (D >= 128) __builtin_amdgcn_sched_barrier(0);  // as in the dQ kernel
       }
     };
-    if (masked)
+    // (at d = 128 without the causal mask the compiler's schedule of a second,
+    // unmasked copy of the tile body spills, so there every tile takes the
+    // masked one)
+    if ((D >= 128 && !CAUSAL) || masked)
       scores(std::true_type{});
     else
       scores(std::false_type{});
