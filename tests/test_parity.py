@@ -113,6 +113,27 @@ def test_rows_sum_to_one_minus_lambda(dev, dtype, lam):
     assert np.max(np.abs(out - (1.0 - lam))) <= tol
 
 
+@pytest.mark.parametrize("H", [3, 12])
+def test_prefill_every_row_long_causal(dev, H):
+    """Every row of a long causal prefill is written: 16384 tokens are 128
+    query tiles of 128 rows, which on a 256-CU part the prefill deals out per
+    XCD (chunks of 32 query tiles of one head to the 32 workgroups of an
+    XCD; 12 and 48 chunks here).  The output starts as NaN; with V = ones and
+    no norm each row of Y is 1 - lambda (each map's weights sum to one), so a
+    row that no item wrote shows.  (Which keys a row saw is what the sampled
+    rows of the full-size cases check against the oracle.)"""
+    print(f"case every-row causal B=1 H={H} N=16384 d=128", flush=True)
+    x = _to(W.prefill_inputs(1, H, 16384, 128, "bf16", seed=40 + H), dev)
+    x["v"] = torch.ones_like(x["v"])
+    lam = 0.37
+    lam_t = torch.tensor([lam], dtype=torch.float32, device=dev)
+    out = torch.full_like(x["v"], float("nan"))
+    da.fwd(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam_t, x["lambda_init"], causal=True, norm=False, out=out)
+    torch.cuda.synchronize()
+    err = (out.float() - (1.0 - lam)).abs().max().item()
+    assert err <= 4e-3, err
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_six_key_example(dev, dtype):
     # page "Differential attention", section "The noise-canceling idea":

@@ -229,7 +229,8 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
   // the same key tiles through that XCD's L2 at about the same time (rather
   // than each L2 serving the key streams of several heads).  Chunks go
   // longest first, heads fastest, chunk c of the order to XCD c % 8 in round
-  // c / 8; within a chunk workgroup j takes tile j, or W-1-j in odd rounds,
+  // c / 8 (to XCD 7 - c % 8 in odd rounds, so that the XCDs' totals even
+  // out); within a chunk workgroup j takes tile j, or W-1-j in odd rounds,
   // so that the totals of an XCD's workgroups even out.
   const int G = gridDim.x, g = blockIdx.x, BH = a.BH;
   const int n_items = a.n_qtiles * BH;  // below 2^31 (checked by the host)
@@ -240,7 +241,9 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
       // c / BH without the vector code of an integer division: a multiply
       // by ceil(2^32 / BH) in scalar registers, corrected by one either way
       const uint32_t inv_bh = __builtin_amdgcn_readfirstlane((uint32_t)(0xffffffffu / (uint32_t)BH) + 1u);
-      const int c = r * NXCD + g % NXCD;  // chunk
+      // chunk: XCD x takes chunk 8 r + x in even rounds, 8 r + 7 - x in odd
+      // ones, so every XCD's chunks add up to the same number of key tiles
+      const int c = r * NXCD + ((r & 1) ? NXCD - 1 - g % NXCD : g % NXCD);
       if (c >= n_items / W) return -1;
       int kk = (int)__umulhi((uint32_t)c, inv_bh);
       kk -= kk * BH > c ? 1 : 0;
