@@ -113,17 +113,20 @@ def test_rows_sum_to_one_minus_lambda(dev, dtype, lam):
     assert np.max(np.abs(out - (1.0 - lam))) <= tol
 
 
-@pytest.mark.parametrize("H", [3, 12])
-def test_prefill_every_row_long_causal(dev, H):
-    """Every row of a long causal prefill is written: 16384 tokens are 128
-    query tiles of 128 rows, which on a 256-CU part the prefill deals out per
-    XCD (chunks of 32 query tiles of one head to the 32 workgroups of an
-    XCD; 12 and 48 chunks here).  The output starts as NaN; with V = ones and
-    no norm each row of Y is 1 - lambda (each map's weights sum to one), so a
-    row that no item wrote shows.  (Which keys a row saw is what the sampled
-    rows of the full-size cases check against the oracle.)"""
-    print(f"case every-row causal B=1 H={H} N=16384 d=128", flush=True)
-    x = _to(W.prefill_inputs(1, H, 16384, 128, "bf16", seed=40 + H), dev)
+@pytest.mark.parametrize("B,H,N", [(1, 3, 16384), (1, 12, 16384), (2, 12, 4096), (1, 5, 4096)])
+def test_prefill_every_row_causal_schedules(dev, B, H, N):
+    """Every row of a causal prefill is written, under each of the
+    persistent schedules a 256-CU part picks: 16384 tokens are 128 query
+    tiles of 128 rows, dealt out per XCD (chunks of 32 query tiles of one
+    head to the 32 workgroups of an XCD; 12 and 48 chunks here); B=2, H=12,
+    N=4096 is 768 items, exactly three rounds, whose last three rounds take
+    the three-permutation order; B=1, H=5, N=4096 is 160 items, fewer than
+    one round.  The output starts as NaN; with V = ones and no norm each row
+    of Y is 1 - lambda (each map's weights sum to one), so a row that no
+    item wrote shows.  (Which keys a row saw is what the sampled rows of the
+    full-size cases check against the oracle.)"""
+    print(f"case every-row causal B={B} H={H} N={N} d=128", flush=True)
+    x = _to(W.prefill_inputs(B, H, N, 128, "bf16", seed=40 + H + N), dev)
     x["v"] = torch.ones_like(x["v"])
     lam = 0.37
     lam_t = torch.tensor([lam], dtype=torch.float32, device=dev)

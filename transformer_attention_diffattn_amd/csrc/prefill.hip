@@ -255,7 +255,19 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
     } else {
       // integer division expands to vector code: keep the result scalar
       const int alt = __builtin_amdgcn_readfirstlane((G % BH == 0) ? ((G / BH - 1 - g / BH) * BH + g % BH) : (G - 1 - g));
-      const int i = r * G + ((r & 1) ? alt : g);
+      int x = (r & 1) ? alt : g;
+      // An odd number R >= 3 of whole rounds: alternating directions leave
+      // the last round's spread (item lengths fall about linearly with the
+      // item index), so the last three rounds take positions g, (g + G/2 - 1)
+      // mod G and G - 1 - 2g (g < G/2), 0 (g = G/2), 2G - 2g (g > G/2): three
+      // permutations of 0..G-1 whose sum is G + G/2 - 2 or G + G/2 - 1 for
+      // every g (G even).
+      const int R = __builtin_amdgcn_readfirstlane(n_items / G);
+      if (n_items == R * G && (R & 1) && R >= 3 && !(G & 1) && r >= R - 3) {
+        const int h = G / 2, k = r - (R - 3);
+        x = k == 0 ? g : k == 1 ? (g + h - 1) % G : g < h ? G - 1 - 2 * g : g == h ? 0 : 2 * G - 2 * g;
+      }
+      const int i = r * G + x;
       return __builtin_amdgcn_readfirstlane(i < n_items ? i : -1);
     }
   };
