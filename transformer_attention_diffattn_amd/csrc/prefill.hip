@@ -234,6 +234,29 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
   // so that the totals of an XCD's workgroups even out.
   const int G = gridDim.x, g = blockIdx.x, BH = a.BH;
   const int n_items = a.n_qtiles * BH;  // below 2^31 (checked by the host)
+  // An odd number R >= 3 of whole rounds: alternating directions leave the
+  // last round's spread (item lengths fall about linearly with the item
+  // index), so the last three rounds take the three permutations P_k of
+  // 0..n-1 (n even, h = n/2): P_0(v) = v, P_1(v) = (v + h - 1) mod n,
+  // P_2(v) = n - 1 - 2v (v < h), 0 (v = h), 2n - 2v (v > h), whose sum is
+  // n + h - 2 or n + h - 1 for every v.  With G a multiple of 16 they act on
+  // g / 8 and g % 8 apart (position 8 P_k(g / 8) + P_k(g % 8)), which keeps
+  // every XCD's items of a round on a few heads (a head's items differ by
+  // multiples of B*H, and XCD = g % 8).  Positions 1 and 2 of this
+  // workgroup, computed once.
+  // (scalar registers: the grid size arrives through a vector load, and the
+  // values live through the whole kernel)
+  const int R_all = __builtin_amdgcn_readfirstlane(n_items / G);
+  const bool tail3 = __builtin_amdgcn_readfirstlane(n_items == R_all * G && (R_all & 1) && R_all >= 3 && !(G & 1));
+  const int R3 = R_all - 3;
+  auto tail_perm = [](int k, int v, int n) {  // (no division: v + h - 1 < 2n)
+    const int h = n / 2, w = v + h - 1;
+    return k == 1 ? (w >= n ? w - n : w) : v < h ? n - 1 - 2 * v : v == h ? 0 : 2 * n - 2 * v;
+  };
+  const int tail_pos1 = __builtin_amdgcn_readfirstlane(
+      (G % 16 == 0) ? 8 * tail_perm(1, g / 8, G / 8) + tail_perm(1, g % 8, 8) : tail_perm(1, g, G));
+  const int tail_pos2 = __builtin_amdgcn_readfirstlane(
+      (G % 16 == 0) ? 8 * tail_perm(2, g / 8, G / 8) + tail_perm(2, g % 8, 8) : tail_perm(2, g, G));
   auto item_at = [&](int r) -> int {
     if constexpr (XCD) {
       constexpr int NXCD = 8;
@@ -256,16 +279,11 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
       // integer division expands to vector code: keep the result scalar
       const int alt = __builtin_amdgcn_readfirstlane((G % BH == 0) ? ((G / BH - 1 - g / BH) * BH + g % BH) : (G - 1 - g));
       int x = (r & 1) ? alt : g;
-      // An odd number R >= 3 of whole rounds: alternating directions leave
-      // the last round's spread (item lengths fall about linearly with the
-      // item index), so the last three rounds take positions g, (g + G/2 - 1)
-      // mod G and G - 1 - 2g (g < G/2), 0 (g = G/2), 2G - 2g (g > G/2): three
-      // permutations of 0..G-1 whose sum is G + G/2 - 2 or G + G/2 - 1 for
-      // every g (G even).
-      const int R = __builtin_amdgcn_readfirstlane(n_items / G);
-      if (n_items == R * G && (R & 1) && R >= 3 && !(G & 1) && r >= R - 3) {
-        const int h = G / 2, k = r - (R - 3);
-        x = k == 0 ? g : k == 1 ? (g + h - 1) % G : g < h ? G - 1 - 2 * g : g == h ? 0 : 2 * G - 2 * g;
+      if (tail3 && r >= R3) {
+        // (arithmetic, not a chain of selects: the compiler turns such a
+        // chain into a small indexed table in memory)
+        const int k = r - R3;
+        x = g + (k == 1 ? 1 : 0) * (tail_pos1 - g) + (k == 2 ? 1 : 0) * (tail_pos2 - g);
       }
       const int i = r * G + x;
       return __builtin_amdgcn_readfirstlane(i < n_items ? i : -1);
