@@ -72,7 +72,9 @@ def test_out_proj(dev, B, H, N, d, dout):
 # shapes large enough for the 256 x 256 large-tile form (reduction a multiple
 # of 64), with ragged token and feature edges and workgroups past the tile
 # grid: every element against the oracle
-@pytest.mark.parametrize("B,N,dm,H,d", [(1, 3000, 512, 8, 64), (2, 2100, 256, 6, 128)])
+# (1, 2048, 256, 25, 64): 9600 features, whose large-tile blocks make one and
+# a quarter rounds, so the last 1408 features go to the 128 x 128 form
+@pytest.mark.parametrize("B,N,dm,H,d", [(1, 3000, 512, 8, 64), (2, 2100, 256, 6, 128), (1, 2048, 256, 25, 64)])
 def test_in_proj_large_tiles_ragged(dev, B, N, dm, H, d):
     print(f"case in_proj large B={B} N={N} d_model={dm} H={H} d={d}", flush=True)
     x = W.projection_inputs(B, N, dm, H, d, seed=970 + N)
@@ -84,7 +86,9 @@ def test_in_proj_large_tiles_ragged(dev, B, N, dm, H, d):
         _check(g, r, m, dm)
 
 
-@pytest.mark.parametrize("B,H,N,d,dout", [(1, 8, 8300, 32, 1000), (2, 4, 4150, 64, 1028)])
+# (1, 4, 8192, 64, 2600): blocks making one and a half rounds; features
+# 2048..2599 (a ragged 128-tile at the end) go to the 128 x 128 form
+@pytest.mark.parametrize("B,H,N,d,dout", [(1, 8, 8300, 32, 1000), (2, 4, 4150, 64, 1028), (1, 4, 8192, 64, 2600)])
 def test_out_proj_large_tiles_ragged(dev, B, H, N, d, dout):
     print(f"case out_proj large B={B} H={H} N={N} d={d} d_out={dout}", flush=True)
     x = W.projection_inputs(B, N, 64, H, d, seed=990 + N, d_out=dout)

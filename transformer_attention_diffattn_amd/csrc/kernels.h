@@ -87,6 +87,7 @@ struct ProjArgs {
   int F;            // output features (multiple of 4)
   int N, H;
   int log2_dv;      // log2(2d)
+  int f_lo, f_hi;   // output features [f_lo, f_hi) of one launch (set by launch_proj)
 };
 
 // mode 0: in-projection, 1: out-projection

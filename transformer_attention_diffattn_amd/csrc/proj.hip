@@ -54,7 +54,7 @@ __global__ __launch_bounds__(256, 2) void proj_kernel(ProjArgs a) {
   const int gm = min(nMt - first_m, GM);
   const int rem = seq - grp * GM * nF;
   const int tile_m = first_m + rem % gm, tile_f = rem / gm;
-  const int n0 = tile_f * kProjTile + (wave & 1) * 64;  // output features
+  const int n0 = a.f_lo + tile_f * kProjTile + (wave & 1) * 64;  // output features
   const int m0 = tile_m * kProjTile + (wave >> 1) * 64;  // tokens (M < 2^23)
   const int K = a.K, F = a.F, M = a.M, N = a.N, H = a.H;
   const int l2dv = a.log2_dv;  // 2d = 1 << l2dv (out-projection reads; in-projection writes)
@@ -67,7 +67,7 @@ __global__ __launch_bounds__(256, 2) void proj_kernel(ProjArgs a) {
   // consecutive threads cover one row's 128 bytes.
   __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][kProjTile * 64];  // [buffer][W, X][row*64 + k]
   const int tid = threadIdx.x;
-  const int wf0 = tile_f * kProjTile, wm0 = tile_m * kProjTile;  // workgroup's first feature / token
+  const int wf0 = a.f_lo + tile_f * kProjTile, wm0 = tile_m * kProjTile;  // workgroup's first feature / token
   const uint16_t* wsrc[4];
   const uint16_t* xsrc[4];
   int lrow[4], lchk[4];
@@ -229,7 +229,8 @@ __global__ __launch_bounds__(512, 1) void proj256_kernel(ProjArgs a) {
   // tile order (see above); the grid covers whole rounds of 8 XCD blocks,
   // and a workgroup whose block or tile lies past the tile grid has nothing
   // to do (it leaves before any barrier)
-  const int nFt = (F + kBigTile - 1) / kBigTile, nMt = (M + kBigTile - 1) / kBigTile;
+  // (this form always starts at feature 0: f_lo = 0, f_hi = F or a multiple of 256)
+  const int nFt = (a.f_hi + kBigTile - 1) / kBigTile, nMt = (M + kBigTile - 1) / kBigTile;
   const int nFb = (nFt + kBigFB - 1) / kBigFB, nMb = (nMt + kBigMB - 1) / kBigMB;
   const int L = blockIdx.x;
   const int bi = (L % 8) + 8 * ((L / 8) / (kBigFB * kBigMB));  // XCD block
@@ -371,31 +372,67 @@ __global__ __launch_bounds__(512, 1) void proj256_kernel(ProjArgs a) {
 
 // The large-tile form needs a reduction length that is a multiple of 64 and
 // a head width of at least 64 when it reads the per-head attention output;
-// it pays for large products only (at least one full round of XCD blocks).
-// Its grid: whole rounds of 8 XCD blocks of 4 x 8 tiles of 256.
-static long long proj256_grid(int mode, const ProjArgs& a) {
-  if (a.K % 64 != 0 || (mode == 1 && a.log2_dv < 6)) return 0;
+// it pays for large products only (at least half a round of XCD blocks).
+// Its grid: whole rounds of 8 XCD blocks of 4 x 8 tiles of 256, over the
+// features [0, f_hi).
+static bool proj256_fits(int mode, const ProjArgs& a) {
+  if (a.K % 64 != 0 || (mode == 1 && a.log2_dv < 6)) return false;
   const long long nFt = (a.F + kBigTile - 1) / kBigTile, nMt = (a.M + kBigTile - 1) / kBigTile;
+  return nFt * nMt >= 8LL * kBigFB * kBigMB / 2;
+}
+static long long proj256_grid(const ProjArgs& a) {
+  const long long nFt = (a.f_hi + kBigTile - 1) / kBigTile, nMt = (a.M + kBigTile - 1) / kBigTile;
   const long long blocks = ((nFt + kBigFB - 1) / kBigFB) * ((nMt + kBigMB - 1) / kBigMB);
-  if (nFt * nMt < 8LL * kBigFB * kBigMB / 2) return 0;
   return (blocks + 7) / 8 * 8 * kBigFB * kBigMB;
 }
 
-hipError_t launch_proj(int mode, const ProjArgs& a, hipStream_t stream) {
-  const long long g256 = proj256_grid(mode, a);
-  if (g256 > 0) {
-    const unsigned grid = (unsigned)g256;
-    if (mode == 0)
-      hipLaunchKernelGGL(proj256_kernel<0>, dim3(grid), dim3(512), 0, stream, a);
-    else
-      hipLaunchKernelGGL(proj256_kernel<1>, dim3(grid), dim3(512), 0, stream, a);
-    return hipGetLastError();
-  }
-  const dim3 grid((unsigned)((a.F + kProjTile - 1) / kProjTile), (unsigned)((a.M + kProjTile - 1) / kProjTile));
+// Features of the large-tile launch.  When its XCD blocks make a last round
+// that is only partly filled, the features of the blocks past the last
+// whole round (whole feature blocks of 1024) go to the 128 x 128 form
+// instead, in a second launch, if that takes less time than the partial
+// round: the 128 x 128 form runs at about 0.7 of the large one's rate and
+// fills all compute units with two workgroups each.
+static int proj256_features(const ProjArgs& a) {
+  const long long nFt = (a.F + kBigTile - 1) / kBigTile, nMt = (a.M + kBigTile - 1) / kBigTile;
+  const long long nFb = (nFt + kBigFB - 1) / kBigFB, nMb = (nMt + kBigMB - 1) / kBigMB;
+  const long long per_round = 8LL * kBigFB * kBigMB;  // tiles of 256 per round
+  if ((nFb * nMb) % 8 == 0) return a.F;
+  long long nf = nFb - 1;
+  while (nf >= 1 && (nf * nMb) % 8 != 0) --nf;
+  if (nf < 1) return a.F;
+  const long long rounds_full = (nFb * nMb + 7) / 8, rounds_big = nf * nMb / 8;
+  const double rest_rounds = (double)(nFt - nf * kBigFB) * (double)nMt / (double)per_round;
+  if (rest_rounds / 0.7 >= (double)(rounds_full - rounds_big) - 0.05) return a.F;
+  return (int)(nf * kBigFB * kBigTile);
+}
+
+static void launch_proj128(int mode, const ProjArgs& a, hipStream_t stream) {
+  const dim3 grid((unsigned)((a.F - a.f_lo + kProjTile - 1) / kProjTile), (unsigned)((a.M + kProjTile - 1) / kProjTile));
   if (mode == 0)
     hipLaunchKernelGGL(proj_kernel<0>, grid, dim3(256), 0, stream, a);
   else
     hipLaunchKernelGGL(proj_kernel<1>, grid, dim3(256), 0, stream, a);
+}
+
+hipError_t launch_proj(int mode, const ProjArgs& args, hipStream_t stream) {
+  ProjArgs a = args;
+  a.f_lo = 0;
+  a.f_hi = a.F;
+  if (proj256_fits(mode, a)) {
+    a.f_hi = proj256_features(a);
+    const unsigned grid = (unsigned)proj256_grid(a);
+    if (mode == 0)
+      hipLaunchKernelGGL(proj256_kernel<0>, dim3(grid), dim3(512), 0, stream, a);
+    else
+      hipLaunchKernelGGL(proj256_kernel<1>, dim3(grid), dim3(512), 0, stream, a);
+    if (a.f_hi < a.F) {
+      a.f_lo = a.f_hi;
+      a.f_hi = a.F;
+      launch_proj128(mode, a, stream);
+    }
+    return hipGetLastError();
+  }
+  launch_proj128(mode, a, stream);
   return hipGetLastError();
 }
 
