@@ -135,6 +135,27 @@ def test_backward_without_weight_and_lambda_zero(dev):
              ("dq1", "dk1", "dv", "dweight"))
 
 
+def test_training_forward_every_row_3b_shape(dev):
+    """Every row of the training forward at the 3B layer's shape is written,
+    with its saved per-map outputs and log-sum-exps (768 items of 128 rows:
+    exactly three rounds of a 256-CU part, whose last three take the
+    three-permutation order).  With V = ones each map's output O_k is 1 in
+    every channel, and the normalised output is (1 - lambda_init) (1 - lambda)
+    / sqrt((1 - lambda)^2 + eps) (weight ones)."""
+    print("case fwd_train every-row B=2 H=12 N=4096 d=128", flush=True)
+    x = W.prefill_inputs(2, 12, 4096, 128, "bf16", seed=85, device=dev)
+    v = torch.ones_like(x["v"])
+    lam = 0.37
+    lam_t = torch.tensor([lam], dtype=torch.float32, device=dev)
+    out, lse, o12 = da.fwd_train(x["q1"], x["k1"], x["q2"], x["k2"], v, lam_t, x["lambda_init"], eps=x["eps"])
+    torch.cuda.synchronize()
+    assert torch.isfinite(lse).all()
+    assert (o12 - 1.0).abs().max().item() <= 1e-5
+    y = 1.0 - lam
+    want = (1.0 - x["lambda_init"]) * y / math.sqrt(y * y + x["eps"])
+    assert (out.float() - want).abs().max().item() <= 4e-3
+
+
 def test_backward_deterministic(dev):
     x = _inputs(1, 3, 300, 64, seed=21)
     a = _run(x, dev, True)[4]

@@ -194,6 +194,27 @@ def test_fp8qk_rows_sum_to_one_minus_lambda(dev, lam_value):
     assert np.max(np.abs(out - (1.0 - lam_value))) <= 4e-3
 
 
+def test_fp8qk_every_row_3b_shape(dev):
+    """Every row of the fp8 prefill at the 3B layer's shape is written (768
+    items of 128 rows: exactly three rounds of a 256-CU part, whose last three
+    take the three-permutation order): the codes come from the library's own
+    quantiser (any codes do: with V = ones and no norm every row of Y is
+    1 - lambda), and the output starts as NaN."""
+    print("case fp8 every-row B=2 H=12 N=4096 d=128", flush=True)
+    x = W.prefill_inputs(2, 12, 4096, D, "bf16", seed=84, device=dev)
+    xs = [x[k] for k in ("q1", "k1", "q2", "k2")]
+    ws = torch.empty(max(4, 4 * da.quantize_fp8_workspace_bytes(xs[0].numel())), dtype=torch.uint8, device=dev)
+    codes, scales = da.quantize_fp8_batch(xs, workspace=ws)
+    lam = 0.37
+    lam_t = torch.tensor([lam], dtype=torch.float32, device=dev)
+    v = torch.ones_like(x["v"])
+    out = torch.full_like(v, float("nan"))
+    da.fwd_fp8qk(codes[0], codes[1], codes[2], codes[3], scales, v, lam_t, 0.8, causal=True, norm=False, out=out)
+    torch.cuda.synchronize()
+    err = (out.float() - (1.0 - lam)).abs().max().item()
+    assert err <= 4e-3, err
+
+
 @pytest.mark.parametrize("lam_value", [-0.3, 0.0, 1.0])
 def test_fp8qk_lambda_values(dev, lam_value):
     x = W.prefill_inputs(1, 3, 150, D, "bf16", seed=51)
