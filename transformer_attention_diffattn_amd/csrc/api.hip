@@ -42,6 +42,8 @@ namespace diffattn {
 // decode.hip: address of the allocation-free decode's fixed scratch array
 // (DIFFATTN_NOALLOC_SCRATCH_BYTES) on the device that runs `stream`
 hipError_t decode_scratch(hipStream_t stream, float** ptr);
+// backward.hip: columns of per-workgroup partial sums diffattn_bwd writes
+int bwd_partial_count(int BH, int N, int d);
 }  // namespace diffattn
 
 namespace {
@@ -261,7 +263,7 @@ static void bwd_layout(int B, int H, int N, int d, size_t* off_delta, size_t* of
   const size_t rows = (size_t)B * H * N;
   const size_t dy = round256(rows * 2 * d * 2);
   const size_t delta = round256(rows * 2 * 4);
-  const size_t part = round256((size_t)diffattn::bwd_prep_blocks((long long)rows) * (2 * d + 1) * 4);
+  const size_t part = round256((size_t)diffattn::bwd_partial_count(B * H, N, d) * (2 * d + 1) * 4);
   *off_delta = dy;
   *off_part = dy + delta;
   *total = dy + delta + part;

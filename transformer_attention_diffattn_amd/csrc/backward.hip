@@ -281,12 +281,17 @@ template <int D>
 struct DqCfg {
   static constexpr int SUB = D <= 64 ? 2 : 1;
   static constexpr int ROWS = 4 * 16 * SUB;  // query rows per workgroup
+  // d <= 64: the dQ kernel also does the row-wise preparation of its rows
+  // (no bwd_prep_kernel launch); d = 128 keeps the separate kernel, whose
+  // per-row values would not fit beside the dQ kernel's registers
+  static constexpr bool FUSE_PREP = D <= 64;
 };
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   constexpr int DV = 2 * D, KS = D / 32, KV = DV / 32, DB = D / 16, BN = kDqKeys;
   constexpr int SUB = DqCfg<D>::SUB, ROWS = DqCfg<D>::ROWS;
+  constexpr bool FUSE = DqCfg<D>::FUSE_PREP;
   static_assert(BN == kTileRows, "one load instruction per 32-row column block");
   constexpr int STAGE = 2 * BN * D + BN * DV;  // K1, K2, V tiles
   constexpr int NI = D / 16;                   // load instructions per wave and tile
@@ -316,21 +321,162 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   int q[SUB];
   bf16x8 qf1[SUB][KS], qf2[SUB][KS], dyf[SUB][KV];
   float lse1[SUB], lse2[SUB], dl1[SUB], dl2[SUB];
+  // the first key tiles load while the rows are prepared
+  const int kend = CAUSAL ? min(N, q0 + ROWS) : N;
+  const int nkt = (kend + BN - 1) / BN;
+  // segments of a stage: the D/16 column blocks of K1, then of K2, then
+  // the D/8 of V; wave w issues segments w, w + 4, ...
+  const uint32_t lds0 = lds_offset(stg);
+  auto issue = [&](int kt) {
+    const uint32_t base = lds0 + 2u * (uint32_t)((kt % kStages) * STAGE);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int sg = wave + 4 * i;
+      if (sg < D / 16)
+        dma_block(K1, D, sg, kt * BN, N, lane, base + 1024u * sg);
+      else if (sg < D / 8)
+        dma_block(K2, D, sg - D / 16, kt * BN, N, lane, base + 2u * BN * D + 1024u * (sg - D / 16));
+      else
+        dma_block(V, DV, sg - D / 8, kt * BN, N, lane, base + 4u * BN * D + 1024u * (sg - D / 8));
+    }
+  };
+  issue(0);
+  if (kStages == 3 && nkt > 1) issue(1);
+#pragma unroll
+  for (int u = 0; u < SUB; ++u) q[u] = qw + 16 * u + lr;
+  if constexpr (FUSE) {
+    // The row-wise preparation of this workgroup's query rows (what
+    // bwd_prep_kernel does for the other head widths), on the channels this
+    // lane holds as dY B operands: 32 kv + 8 lg .. + 7 for kv < 2d/32, the
+    // four lanes of equal lr covering the row.  dY and the deltas also go
+    // to the workspace for the dK/dV kernel; the norm-weight and dlambda
+    // sums of the workgroup's rows go to its column of the partials.
+    const float sigma = a.out_scale;
+    float dwp[KV][8];
+#pragma unroll
+    for (int kv = 0; kv < KV; ++kv)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dwp[kv][e] = 0.f;
+    float dlp = 0.f;
+#pragma unroll
+    for (int u = 0; u < SUB; ++u) {
+      const bool valid = q[u] < N;
+      const size_t row = hb + (size_t)min(q[u], N - 1);
+      float x1[KV][8], x2[KV][8], gd[KV][8];
+#pragma unroll
+      for (int kv = 0; kv < KV; ++kv) {
+        const int ch = 32 * kv + 8 * lg;
+        const f32x4* o1 = reinterpret_cast<const f32x4*>(a.osave + row * DV + ch);
+        const f32x4* o2 = reinterpret_cast<const f32x4*>(a.osave + (nrows + row) * DV + ch);
+        const f32x4 p0 = o1[0], p1 = o1[1], r0 = o2[0], r1 = o2[1];
+        const u32x4 g = ld16((const uint16_t*)a.dout + row * DV + ch);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x1[kv][i] = p0[i];
+          x1[kv][4 + i] = p1[i];
+          x2[kv][i] = r0[i];
+          x2[kv][4 + i] = r1[i];
+          gd[kv][2 * i] = bf16_lo(g[i]);
+          gd[kv][2 * i + 1] = bf16_hi(g[i]);
+        }
+      }
+      // the norm weight of channel c (read where used, not kept)
+      auto wch = [&](int c) { return a.norm_w ? a.norm_w[c] : 1.0f; };
+      float y[KV][8], ss = 0.f, gy = 0.f;
+#pragma unroll
+      for (int kv = 0; kv < KV; ++kv)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          y[kv][e] = x1[kv][e] - lam * x2[kv][e];
+          ss += y[kv][e] * y[kv][e];
+          gy += sigma * wch(32 * kv + 8 * lg + e) * gd[kv][e] * y[kv][e];
+        }
+      // the row's four lanes: lg = lane / 16
+      ss += __shfl_xor(ss, 16);
+      ss += __shfl_xor(ss, 32);
+      gy += __shfl_xor(gy, 16);
+      gy += __shfl_xor(gy, 32);
+      const float ir = 1.0f / sqrtf(ss * (1.0f / DV) + a.eps);
+      const float k3 = gy * ir * ir * ir * (1.0f / DV);
+      // delta_k from dY as rounded to bf16 (the dY the products see), so that
+      // dP - delta cancels where it should; dlambda from the fp32 dY
+      float t1 = 0.f, t2 = 0.f, u2 = 0.f;
+#pragma unroll
+      for (int kv = 0; kv < KV; ++kv) {
+        uint32_t pk[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int ch = 32 * kv + 8 * lg + 2 * i;
+          const float d0 = sigma * wch(ch) * gd[kv][2 * i] * ir - y[kv][2 * i] * k3;
+          const float d1 = sigma * wch(ch + 1) * gd[kv][2 * i + 1] * ir - y[kv][2 * i + 1] * k3;
+          pk[i] = pack_bf16x2(d0, d1);
+          const float q0r = bf16_lo(pk[i]), q1r = bf16_hi(pk[i]);
+          t1 += q0r * x1[kv][2 * i] + q1r * x1[kv][2 * i + 1];
+          t2 += q0r * x2[kv][2 * i] + q1r * x2[kv][2 * i + 1];
+          u2 += d0 * x2[kv][2 * i] + d1 * x2[kv][2 * i + 1];
+        }
+        const u32x4 pv = {pk[0], pk[1], pk[2], pk[3]};
+        dyf[u][kv] = as_bf16x8(pv);
+        if (valid) st16(a.dy + row * DV + 32 * kv + 8 * lg, pv);
+        if (valid) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) dwp[kv][e] += sigma * gd[kv][e] * y[kv][e] * ir;
+        }
+      }
+      t1 += __shfl_xor(t1, 16);
+      t1 += __shfl_xor(t1, 32);
+      t2 += __shfl_xor(t2, 16);
+      t2 += __shfl_xor(t2, 32);
+      u2 += __shfl_xor(u2, 16);
+      u2 += __shfl_xor(u2, 32);
+      dl1[u] = t1;
+      dl2[u] = -lam * t2;
+      if (valid && lg == 0) {
+        a.delta[row] = dl1[u];
+        a.delta[nrows + row] = dl2[u];
+        dlp -= u2;
+      }
+    }
+    // this workgroup's sums: over the 16 rows of a lane group (lr), then over
+    // the waves through LDS, in a fixed order
+    __shared__ float sdw[4][DV];
+    __shared__ float sdl[4];
+#pragma unroll
+    for (int kv = 0; kv < KV; ++kv)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) dwp[kv][e] += __shfl_xor(dwp[kv][e], off);
+    dlp = wave_sum(dlp);
+    if (lr == 0) {
+#pragma unroll
+      for (int kv = 0; kv < KV; ++kv)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sdw[wave][32 * kv + 8 * lg + e] = dwp[kv][e];
+    }
+    if (lane == 0) sdl[wave] = dlp;
+    __syncthreads();
+    float* part = a.partial + blockIdx.x;
+    const size_t np = gridDim.x;
+    for (int cix = tid; cix < DV; cix += 256) part[(size_t)cix * np] = ((sdw[0][cix] + sdw[1][cix]) + sdw[2][cix]) + sdw[3][cix];
+    if (tid == 0) part[(size_t)DV * np] = ((sdl[0] + sdl[1]) + sdl[2]) + sdl[3];
+  }
 #pragma unroll
   for (int u = 0; u < SUB; ++u) {
-    q[u] = qw + 16 * u + lr;
     const int qc = min(q[u], N - 1);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       qf1[u][ks] = as_bf16x8(ld16(Q1 + (size_t)qc * D + 32 * ks + 8 * lg));
       qf2[u][ks] = as_bf16x8(ld16(Q2 + (size_t)qc * D + 32 * ks + 8 * lg));
     }
+    if constexpr (!FUSE) {
 #pragma unroll
-    for (int kv = 0; kv < KV; ++kv) dyf[u][kv] = as_bf16x8(ld16(DY + (size_t)qc * DV + 32 * kv + 8 * lg));
+      for (int kv = 0; kv < KV; ++kv) dyf[u][kv] = as_bf16x8(ld16(DY + (size_t)qc * DV + 32 * kv + 8 * lg));
+      dl1[u] = a.delta[hb + qc];
+      dl2[u] = a.delta[nrows + hb + qc];
+    }
     lse1[u] = a.lse[hb + qc];
     lse2[u] = a.lse[nrows + hb + qc];
-    dl1[u] = a.delta[hb + qc];
-    dl2[u] = a.delta[nrows + hb + qc];
   }
 
 #pragma unroll
@@ -356,26 +502,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       dq1[u][db] = zero_f32x4();
       dq2[u][db] = zero_f32x4();
     }
-  const int kend = CAUSAL ? min(N, q0 + ROWS) : N;
-  const int nkt = (kend + BN - 1) / BN;
-  // segments of a stage: the D/16 column blocks of K1, then of K2, then
-  // the D/8 of V; wave w issues segments w, w + 4, ...
-  const uint32_t lds0 = lds_offset(stg);
-  auto issue = [&](int kt) {
-    const uint32_t base = lds0 + 2u * (uint32_t)((kt % kStages) * STAGE);
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int sg = wave + 4 * i;
-      if (sg < D / 16)
-        dma_block(K1, D, sg, kt * BN, N, lane, base + 1024u * sg);
-      else if (sg < D / 8)
-        dma_block(K2, D, sg - D / 16, kt * BN, N, lane, base + 2u * BN * D + 1024u * (sg - D / 16));
-      else
-        dma_block(V, DV, sg - D / 8, kt * BN, N, lane, base + 4u * BN * D + 1024u * (sg - D / 8));
-    }
-  };
-  issue(0);
-  if (kStages == 3 && nkt > 1) issue(1);
   for (int kt = 0; kt < nkt; ++kt) {
     const int k0 = kt * BN;
     // tile kt has landed (with three stages tile kt+1 may still load) for
@@ -713,6 +839,17 @@ __global__ __launch_bounds__(64) void lambda_bwd_kernel(const float* __restrict_
 // ---------------------------------------------------------------------------
 // dispatch
 
+// columns of per-workgroup partial sums the backward writes (one per dQ
+// workgroup where the dQ kernel does the row-wise preparation)
+int bwd_partial_count(int BH, int N, int d) {
+  const long long rows = (long long)BH * N;
+  switch (d) {
+    case 32: return (int)(((N + DqCfg<32>::ROWS - 1) / DqCfg<32>::ROWS) * (long long)BH);
+    case 64: return (int)(((N + DqCfg<64>::ROWS - 1) / DqCfg<64>::ROWS) * (long long)BH);
+    default: return bwd_prep_blocks(rows);
+  }
+}
+
 int bwd_prep_blocks(long long rows) {
   const long long per = kPrepThreads / 64;
   const long long need = (rows + per - 1) / per;
@@ -722,11 +859,19 @@ int bwd_prep_blocks(long long rows) {
 template <int D, bool C>
 static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
   const long long rows = (long long)a.BH * a.N;
-  const int np = bwd_prep_blocks(rows);
-  hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3(np), dim3(kPrepThreads), 0, s, a);
-  hipLaunchKernelGGL(bwd_reduce_kernel, dim3(2 * D + 1), dim3(64), 0, s, a.partial, np, 2 * D + 1, a.dweight, a.dlambda);
   const unsigned gq = (unsigned)(((a.N + DqCfg<D>::ROWS - 1) / DqCfg<D>::ROWS) * (long long)a.BH);
-  hipLaunchKernelGGL((bwd_dq_kernel<D, C>), dim3(gq), dim3(256), 0, s, a);
+  if constexpr (DqCfg<D>::FUSE_PREP) {
+    // dQ first: it writes dY, the deltas and the partial sums
+    hipLaunchKernelGGL((bwd_dq_kernel<D, C>), dim3(gq), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(bwd_reduce_kernel, dim3(2 * D + 1), dim3(64), 0, s, a.partial, (int)gq, 2 * D + 1, a.dweight,
+                       a.dlambda);
+  } else {
+    const int np = bwd_prep_blocks(rows);
+    hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3(np), dim3(kPrepThreads), 0, s, a);
+    hipLaunchKernelGGL(bwd_reduce_kernel, dim3(2 * D + 1), dim3(64), 0, s, a.partial, np, 2 * D + 1, a.dweight,
+                       a.dlambda);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, C>), dim3(gq), dim3(256), 0, s, a);
+  }
   const unsigned gk = (unsigned)(((a.N + kDkvKeys - 1) / kDkvKeys) * (long long)a.BH);
   if constexpr (D >= 128) {
     hipLaunchKernelGGL((bwd_dkv_kernel<D, C, 1>), dim3(gk), dim3(256), 0, s, a);
