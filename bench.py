@@ -324,7 +324,10 @@ where dV and dK are also computed apart)."""
         "executed_flops_per_pair": 28 * w.d, "tflops": round(achieved, 2),
         "fwd_train_ms": round(fms, 4),
         "fwd_train_tflops": round(12.0 * w.d * w.pairs() * w.B * w.H / (fms * 1e-3) / 1e12, 2),
-        "roofline": {"bound": "mfma", "kernel": f"bwd_prep + bwd_reduce + bwd_dq + bwd_dkv <{w.d},{'causal' if w.causal else 'full'}>",
+        # (at d <= 64 the dQ kernel also does the row-wise preparation)
+        "roofline": {"bound": "mfma",
+                     "kernel": ("" if w.d <= 64 else "bwd_prep + ") + "bwd_dq + bwd_reduce + bwd_dkv "
+                               f"<{w.d},{'causal' if w.causal else 'full'}>",
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": (_traffic("backward_layer1p4b", "backward.hip")
