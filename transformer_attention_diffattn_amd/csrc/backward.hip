@@ -19,7 +19,8 @@
 // of the scaled scores and O_k; A_k is recomputed here as
 // 2^(s log2(e)/sqrt(d) - lse_k).  The launches:
 //   bwd_prep_kernel    row-wise: Y, r, dY (bf16), delta1, delta2, and per-
-//                      workgroup partial sums of dw and dlambda;
+//                      workgroup partial sums of dw and dlambda (d = 128;
+//                      at d <= 64 the dQ kernel does this for its own rows);
 //   bwd_reduce_kernel  the partial sums in a fixed order (deterministic);
 //   bwd_dq_kernel      query-parallel: S^T, dP^T and dQ^T += K^T dS^T;
 //   bwd_dkv_kernel     key-parallel: S, dP and dV^T += dY^T D,
