@@ -495,6 +495,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     settle(dl2[u]);
   }
 
+  // the dP products start from -delta1 and so deliver dP - delta1; then
+  // -lambda dP - delta2 = -lambda (dP - delta1) - (lambda delta1 + delta2)
+  float nd1[SUB], c2[SUB];
+#pragma unroll
+  for (int u = 0; u < SUB; ++u) {
+    nd1[u] = -dl1[u];
+    c2[u] = lam * dl1[u] + dl2[u];
+  }
   f32x4 dq1[SUB][DB], dq2[SUB][DB];
 #pragma unroll
   for (int u = 0; u < SUB; ++u)
@@ -531,7 +539,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       for (int kb = 0; kb < 2; ++kb) {
         f32x4 s1[SUB], s2[SUB], dp[SUB];
 #pragma unroll
-        for (int u = 0; u < SUB; ++u) s1[u] = s2[u] = dp[u] = zero_f32x4();
+        for (int u = 0; u < SUB; ++u) {
+          s1[u] = s2[u] = zero_f32x4();
+          dp[u] = f32x4{nd1[u], nd1[u], nd1[u], nd1[u]};
+        }
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           const bf16x8 a1 = as_bf16x8(ld16(sk1 + boff<BN>(16 * kb + lr, 32 * ks + 8 * lg)));
@@ -556,8 +567,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
             const bool ok = !MASK || (key < N && q[u] < N && (!CAUSAL || key <= q[u]));
             const float e1 = ok ? exp2_fast(s1[u][j] * c - lse1[u]) : 0.f;
             const float e2 = ok ? exp2_fast(s2[u][j] * c - lse2[u]) : 0.f;
-            g1[u][kb][j] = e1 * (dp[u][j] - dl1[u]);
-            g2[u][kb][j] = e2 * (-lam * dp[u][j] - dl2[u]);
+            g1[u][kb][j] = e1 * dp[u][j];
+            g2[u][kb][j] = e2 * (-lam * dp[u][j] - c2[u]);
           }
         // at d = 128, keep the next block's fragment reads from being hoisted
         // here: all of a tile's fragments live at once would not fit
