@@ -137,6 +137,37 @@ def test_prefill_every_row_causal_schedules(dev, B, H, N):
     assert err <= 4e-3, err
 
 
+@pytest.mark.parametrize("B,H,N", [(1, 6, 16384), (1, 7, 16384), (1, 5, 32768), (1, 9, 32768), (1, 12, 16384)])
+def test_prefill_long_schedules_sampled_rows(dev, B, H, N):
+    """Long causal contexts whose schedule the host picks per shape: 6 and
+    7 heads of 16384 tokens would make three and a half rounds of per-XCD
+    chunks, too uneven, so the item-wise order runs; 5 and 9 heads of 32768
+    make five and nine rounds, uneven but within the margin the shared key
+    streams buy, and 12 heads of 16384 six even ones: per XCD.  Sampled rows
+    of every head against the oracle, so that an item given to the wrong
+    head or query tile shows."""
+    print(f"case long-schedule sampled rows B={B} H={H} N={N} d=128", flush=True)
+    x = W.prefill_inputs(B, H, N, 128, "bf16", seed=70 + H + N // 1024, device=dev)
+    lam_t = da.lam(x["lq1"], x["lk1"], x["lq2"], x["lk2"], x["lambda_init"])
+    out = da.fwd(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam_t, x["lambda_init"], eps=x["eps"],
+                 causal=True)
+    torch.cuda.synchronize()
+    lam = _lam_host({k: (x[k].cpu() if torch.is_tensor(x[k]) else x[k])
+                     for k in ("lq1", "lk1", "lq2", "lk2", "lambda_init")})
+    rng = np.random.default_rng(N + H)
+    worst = 0.0
+    for b in range(B):
+        for h in range(H):
+            rows = np.array(sorted({0, 127, 128, 4095, 4096, N - 1, *rng.integers(0, N, 6).tolist()}))
+            ref = O.forward_rows(*(x[k][b, h].cpu() for k in ("q1", "k1", "q2", "k2", "v")), rows, lam,
+                                 x["lambda_init"], eps=x["eps"], causal=True)
+            got = out[b, h][torch.from_numpy(rows).to(dev)].float().cpu().numpy()
+            assert np.all(np.isfinite(got))
+            worst = max(worst, _maxerr(got, ref))
+    print(f"sampled max|err| = {worst:.3e}", flush=True)
+    assert worst <= 2e-2
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_six_key_example(dev, dtype):
     # page "Differential attention", section "The noise-canceling idea":
