@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libdiffattn.so")
-SOURCES = ["api.hip", "prefill.hip", "decode.hip", "backward.hip", "quant.hip", "proj.hip"]
+SOURCES = ["api.hip", "prefill.hip", "schedule.hip", "decode.hip", "backward.hip", "quant.hip", "proj.hip"]
 ARCH = "gfx950"
 
 # Packed-fp32 instructions are switched off for all device code.
