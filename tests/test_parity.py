@@ -168,6 +168,32 @@ def test_prefill_long_schedules_sampled_rows(dev, B, H, N):
     assert worst <= 2e-2
 
 
+def test_prefill_longest_head_bf16(dev):
+    """The longest bf16 head the ABI takes at d = 128: 4,194,303 tokens, whose
+    N x 2d bf16 outputs (2,147,482,624 bytes) are one store range short of
+    2^31, so the 32-bit output offsets of the last rows come within 512
+    bytes of their limit.  Sampled rows, the last ones among them, against
+    the oracle; one past this length is refused before any launch (the ABI
+    tests)."""
+    B, H, N, d = 1, 1, 4194303, 128
+    print(f"case longest head B={B} H={H} N={N} d={d}", flush=True)
+    x = W.prefill_inputs(B, H, N, d, "bf16", seed=91, device=dev)
+    lam_t = da.lam(x["lq1"], x["lk1"], x["lq2"], x["lk2"], x["lambda_init"])
+    out = da.fwd(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam_t, x["lambda_init"], eps=x["eps"],
+                 causal=True)
+    torch.cuda.synchronize()
+    lam = _lam_host({k: (x[k].cpu() if torch.is_tensor(x[k]) else x[k])
+                     for k in ("lq1", "lk1", "lq2", "lk2", "lambda_init")})
+    rows = np.array([0, 1, 127, 128, 1 << 20, N // 2, N - 129, N - 128, N - 2, N - 1])
+    got = out[0, 0][torch.from_numpy(rows).to(dev)].float().cpu().numpy()
+    del out
+    ref = O.forward_rows(*(x[k][0, 0].cpu() for k in ("q1", "k1", "q2", "k2", "v")), rows, lam,
+                         x["lambda_init"], eps=x["eps"], causal=True)
+    err = _maxerr(got, ref)
+    print(f"longest head: sampled max|err| = {err:.3e}", flush=True)
+    assert np.all(np.isfinite(got)) and err <= 2e-2
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_six_key_example(dev, dtype):
     # page "Differential attention", section "The noise-canceling idea":
