@@ -83,6 +83,22 @@ def test_prefill_small(dev, dtype, d, causal, N):
     assert err <= TOL[dtype], err
 
 
+@pytest.mark.parametrize("B,H,N,d,causal", [(8, 40, 130, 64, True), (3, 37, 300, 128, True),
+                                             (16, 16, 257, 64, False), (4, 48, 129, 128, True)])
+def test_prefill_many_heads(dev, B, H, N, d, causal):
+    """Many heads of few query tiles: more work items than workgroups, in
+    two and a half, one and a third, three and one and a half rounds of the
+    persistent schedule, with the grid a multiple of B*H (16 x 16) or not.
+    Every element against the oracle."""
+    print(f"case many heads B={B} H={H} N={N} d={d} causal={causal}", flush=True)
+    x = W.prefill_inputs(B, H, N, d, "bf16", seed=2000 + B * H + N)
+    out = _gpu_prefill(x, dev, causal=causal)
+    ref = O.forward(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], _lam_host(x), x["lambda_init"],
+                    eps=x["eps"], causal=causal)
+    err = _maxerr(out.float().cpu().numpy(), ref)
+    assert err <= TOL["bf16"], err
+
+
 def test_config_tiny_fp32(dev):
     w = W.WORKLOADS["tiny_fp32_b1h1n128d16"]
     x = W.workload_inputs(w.name)
