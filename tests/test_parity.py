@@ -301,6 +301,24 @@ def test_decode_small(dev, dtype, d):
     assert _maxerr(o, ref) <= TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_decode_with_norm_weight_and_eps(dev, dtype):
+    """The decode merge's epilogue with a non-unit per-channel norm weight
+    and a large eps (review page, "Summary", Eq. 3)."""
+    lens = [300, 2, 129]
+    y = W.decode_inputs(3, 2, 300, 64, dtype, seed=260, cache_len=lens)
+    wt = (0.5 + torch.rand(128, generator=torch.Generator().manual_seed(261))).float()
+    eps = 0.05
+    g = _to(y, dev)
+    lam_t = da.lam(g["lq1"], g["lk1"], g["lq2"], g["lk2"], g["lambda_init"])
+    out = da.decode(g["q1"], g["q2"], g["k1c"], g["k2c"], g["vc"], lam_t, g["lambda_init"],
+                    cache_len=g["cache_len"], weight=wt.to(dev), eps=eps)
+    torch.cuda.synchronize()
+    ref = O.decode(y["q1"][:, :, 0], y["q2"][:, :, 0], y["k1c"], y["k2c"], y["vc"], np.array(lens), _lam_host(y),
+                   y["lambda_init"], weight=wt.numpy(), eps=eps)
+    assert _maxerr(out[:, :, 0].float().cpu().numpy(), ref) <= TOL[dtype]
+
+
 def test_decode_no_cache_len_and_long_cache(dev):
     y = W.decode_inputs(2, 2, 5000, 128, "bf16", seed=210)
     g = _to(y, dev)
