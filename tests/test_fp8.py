@@ -165,6 +165,28 @@ def test_fp8qk_matches_oracle_on_dequantised_inputs(dev, causal, N):
     assert np.all(err <= tol)
 
 
+def test_fp8qk_with_norm_weight(dev):
+    """A non-unit per-channel norm weight (review page, "Summary", Eq. 3):
+    the weight scales each output channel after the norm, so the bound of
+    the unweighted output scales by it channel by channel."""
+    N, causal = 130, True
+    x = W.prefill_inputs(2, 2, N, D, "bf16", seed=5400)
+    codes, scales, deq = _oracle_quant(x)
+    wt = (0.5 + torch.rand(2 * D, generator=torch.Generator().manual_seed(5401))).float()
+    g = {k: torch.from_numpy(codes[k]).to(dev) for k in codes}
+    lam_t = da.lam(*(x[k].to(dev) for k in ("lq1", "lk1", "lq2", "lk2")), x["lambda_init"])
+    got = da.fwd_fp8qk(g["q1"], g["k1"], g["q2"], g["k2"], torch.from_numpy(scales).to(dev), x["v"].to(dev), lam_t,
+                       x["lambda_init"], weight=wt.to(dev), eps=x["eps"], causal=causal).float().cpu().numpy()
+    lam = _lam_host(x)
+    ref = O.forward(deq["q1"], deq["k1"], deq["q2"], deq["k2"], x["v"], lam, x["lambda_init"], weight=wt.numpy(),
+                    eps=x["eps"], causal=causal)
+    tol = _bound(deq["q1"], deq["k1"], deq["q2"], deq["k2"], x["v"], lam, x["lambda_init"], x["eps"], causal,
+                 np.full((2, 2), U_BF16 / np.sqrt(3.0))) * wt.numpy().astype(np.float64)
+    err = np.abs(got - ref)
+    print(f"max err {err.max():.3e}", flush=True)
+    assert np.all(err <= tol)
+
+
 def _gpu_fp8_nonorm(codes, scales, v, lam_value, dev, causal):
     g = {k: torch.from_numpy(codes[k]).to(dev) for k in codes}
     lam_t = torch.tensor([lam_value], dtype=torch.float32, device=dev)
