@@ -618,8 +618,10 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
   // Phase B: P^T of the current tile (bf16, from the exponentials e) with
   // its row sums, and O^T += V^T P^T (V tile at vs) fragment by fragment,
   // each fragment with a slice of the next tile's t = s c - m (masked) and
-  // its row maxima.  Returns whether some row needs a new reference; mt
-  // gets the rows' maxima of t.
+  // its maxima.  Returns whether some row needs a new reference; mt gets
+  // this lane's maxima of t (a row's maximum is that over its four lane
+  // groups, which only the rare rescale needs: the lane maxima already tell
+  // whether any row's exceeds the threshold).
   auto phase_b = [&](const uint16_t* vs, const Scores& e, Scores& sn, int kb, int qw0, float (&mt)[SUB],
                      auto mask_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
@@ -673,17 +675,18 @@ __global__ __launch_bounds__(64 * Bf16Cfg<D>::WAVES) void prefill_bf16_kernel(Pr
     bool need = false;
 #pragma unroll
     for (int u = 0; u < SUB; ++u) {
-      mt[u] = max4_groups(mx[u]);
-      need |= mt[u] > kRescaleThreshold;
+      mt[u] = mx[u];
+      need |= mx[u] > kRescaleThreshold;
     }
     return need;
   };
-  // raise the references of all rows whose t exceeds 0 (t, O, l follow)
+  // raise the references of all rows whose t exceeds 0 (t, O, l follow);
+  // mt: the lanes' maxima of t
   auto rescale_t = [&](Scores& t, const float (&mt)[SUB], bool need) {
     if (wave_any(need)) {
 #pragma unroll
       for (int u = 0; u < SUB; ++u) {
-        const float dm = max_f32(mt[u], 0.0f);
+        const float dm = max_f32(max4_groups(mt[u]), 0.0f);
         const float alpha = exp2_fast(-dm);
         m[u] += dm;
         L[u] *= alpha;
