@@ -36,6 +36,11 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "diff-attn fwd TFLOP/s & % bf16 MFMA peak (prefill); decode HBM GB/s & % peak"
 
 
+# the prefill kernels and the host code that picks their schedule (which
+# decides how the key tiles meet the L2 caches)
+PREFILL_SOURCES = "prefill.hip,schedule.hip"
+
+
 def _traffic(kind: str, src: str):
     """Per-launch HBM bytes from the committed counter summary, if it was
     taken on the current kernel source and headers; else None."""
@@ -147,7 +152,7 @@ def prefill_leg(w, x, steps, warmup, prewarm_s, stream, torch, da, W):
         "roofline": {"bound": "mfma", "kernel": f"prefill_bf16_kernel<{w.d},{'causal' if w.causal else 'full'},norm>",
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": (_traffic(W.PREFILL_TRAFFIC[w.name], "prefill.hip")
+                     "traffic": (_traffic(W.PREFILL_TRAFFIC[w.name], PREFILL_SOURCES)
                                  if w.name in W.PREFILL_TRAFFIC else None),
                      # Q1, K1, Q2, K2 (4d) and V (2d) read once, out (2d) written once: 16 d bytes a row
                      "algorithmic_bytes": 16 * w.d * w.N * w.B * w.H,
@@ -424,7 +429,7 @@ def fp8_leg(args, stream, torch, da, W):
         "roofline": {"bound": "mfma", "kernel": "prefill_bf16_kernel<128,causal,norm,fp8 QK^T>",
                      "achieved": round(achieved, 2), "peak": round(peak, 1), "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4),
-                     "traffic": _traffic("prefill_fp8qk_layer3b", "prefill.hip"),
+                     "traffic": _traffic("prefill_fp8qk_layer3b", PREFILL_SOURCES),
                      "peak_mix": "QK^T 4 d flops/pair at fp8 5033.2, PV 8 d at bf16 2516.6 TFLOP/s"},
         "layer_chain": {"what": "in-projection (%d tokens x %d -> %d) then attention" % (
                             w.B * w.N, w.H * 2 * w.d, 3 * w.H * 2 * w.d),
